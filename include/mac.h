@@ -1,0 +1,214 @@
+/*
+ * libmac: the MAC-Attention decode step (match -> amend -> complete) for
+ * AMD MI355X (gfx950).
+ *
+ * Method source: "MAC-Attention: a Match-Amend-Complete Scheme for Fast and
+ * Accurate Attention Computation", abstract.  Per decode step and query head
+ * the library
+ *   - matches the current pre-RoPE query against the last W cached pre-RoPE
+ *     queries of that head by L2 distance, with a strict threshold tau
+ *     (abstract: the match stage);
+ *   - on a hit reuses the matched entry's cached partial softmax state
+ *     (o, m, l) over its prefix, recomputes the band of B keys at the match
+ *     boundary (abstract: the amend stage) and attends fresh to the KV tail
+ *     (abstract: the complete stage), fusing all partial states with a
+ *     log-sum-exp merge (abstract: "numerically stable merge");
+ *   - on a miss runs full split-K decode attention;
+ *   - pushes the step's own entry (q_pre, prefix state, prefix end, context
+ *     length) into the head's ring, hit or miss.
+ *
+ * Definitions the abstract leaves open, as this library fixes them:
+ *   step order   mac_append_kv stores token n-1, then mac_decode_step attends
+ *                with the query at position n-1 over keys [0, n).
+ *   rotary       rotate-half pairing (i, i + d/2), angle pos * theta^(-2i/d)
+ *                evaluated in double precision; the library rotates q itself,
+ *                keys are stored already rotated.
+ *   state        z = <rope(q), k>/sqrt(d); m = max z, l = sum e^(z-m),
+ *                o = sum e^(z-m) v / l (natural base).  Empty: o=0, m=-inf, l=0.
+ *   entry        the state of the entry's own query over [0, p) with
+ *                p = max(0, n_entry - B).
+ *   match        dist = ||q_pre - entry.q||_2 over entries with
+ *                0 <= entry.p <= p_new; argmin with exact ties to the most
+ *                recent entry; hit iff dist^2 < tau^2 evaluated in fp32.
+ *                NaN distances are never chosen.
+ *   ranges       p_new = max(0, n - B); s = hit ? entry.p : 0;
+ *                prefix = merge(reused, state[s, p_new)), out = merge(prefix,
+ *                state[p_new, n)).o; the pushed entry stores prefix.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are plain HIP device addresses (e.g. from PyTorch
+ *     tensors), 16-byte aligned.  Host pointers are marked "host".
+ *   - Every call enqueues on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronizing.  Stream order is the only
+ *     ordering: call append, then decode, on the same stream.
+ *   - The caller owns every device buffer.  The library never allocates
+ *     device memory.  Ring and workspace are bound at mac_init and must stay
+ *     allocated, and not be touched by the caller, until mac_destroy and
+ *     every enqueued call using them has completed.
+ *   - Errors are returned as mac_status; mac_last_error() gives a message for
+ *     the calling thread.  Argument checks happen before any HIP call, so a
+ *     rejected call enqueues nothing.  A HIP error poisons the context: every
+ *     later call on it returns MAC_ERR_STATE.  Data problems are not errors:
+ *     NaN propagates to the affected head's output, and a NaN distance never
+ *     matches.
+ *   - Calls on one context are not thread-safe; use one context per thread
+ *     or serialize.
+ */
+#ifndef LIBMAC_MAC_H
+#define LIBMAC_MAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAC_OK = 0,
+  MAC_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or value   */
+  MAC_ERR_UNSUPPORTED = 2,  /* valid but not built (head_dim, dtype, G>16)  */
+  MAC_ERR_CAPACITY = 3,     /* a sequence would exceed its KV capacity      */
+  MAC_ERR_DEVICE = 4,       /* a HIP call failed; the message has its code  */
+  MAC_ERR_STATE = 5         /* context poisoned by an earlier device error  */
+} mac_status;
+
+typedef enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 } mac_dtype;
+
+/* Shape and method parameters.  All fields are read at mac_init only. */
+typedef struct {
+  int32_t batch;             /* sequences, >= 1                              */
+  int32_t n_q_heads;         /* Hq, a multiple of n_kv_heads                 */
+  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv must be <= 16              */
+  int32_t head_dim;          /* d: 64 or 128                                 */
+  int32_t dtype;             /* mac_dtype of q, keys, values and ring q      */
+  int32_t max_context;       /* contiguous cache: keys per sequence          */
+  int32_t page_size;         /* 0 = contiguous cache, 16 = paged cache       */
+  int32_t max_pages_per_seq; /* paged: columns of the page table             */
+  int32_t n_pages;           /* paged: pages in the pool                     */
+  int32_t window;            /* W >= 0: ring entries per (sequence, head)    */
+  int32_t band;              /* B >= 0                                       */
+  float tau;                 /* >= 0; hit iff dist < tau (fp32 dist^2 test)  */
+  double rope_theta;         /* > 0                                          */
+  int32_t max_slices;        /* split-K slices per KV group; 0 = default     */
+} mac_config;
+
+typedef struct mac_ctx mac_ctx;
+
+/*
+ * KV cache layout (both contiguous and paged).  Keys and values are stored
+ * in tiles of 16 consecutive token positions of one (sequence, KV head).
+ * Contiguous: tile (b, g, t) starts at element ((b*Hkv + g)*T + t)*16*d with
+ * T = ceil(max_context/16).  Paged (page_size 16): tile t of sequence b is
+ * page page_table[b*max_pages_per_seq + t], at element (page*Hkv + g)*16*d.
+ * Inside a tile the 16 x d elements are permuted so that each 64-lane wave
+ * load of 1 KiB lands directly in matrix-core operand order; the permutation
+ * is private to the library.  Write tokens only with mac_append_kv or
+ * mac_prefill_kv, read them back with mac_read_kv.
+ */
+size_t mac_kv_cache_bytes(const mac_config* cfg);  /* bytes of ONE of K, V   */
+size_t mac_ring_bytes(const mac_config* cfg);      /* opaque ring            */
+size_t mac_workspace_bytes(const mac_config* cfg); /* opaque scratch         */
+
+/*
+ * Create a context.
+ *   ring          device, mac_ring_bytes(cfg); zeroed (emptied) here.
+ *   workspace     device, mac_workspace_bytes(cfg); scratch for a step.
+ *   seq_lens_dev  device int32[batch]: keys stored per sequence.  Device
+ *                 truth, updated by the library's kernels.
+ *   seq_lens_host host int32[batch]: the same lengths now; seeds the host
+ *                 mirror used for capacity checks (no device sync needed).
+ * The ring is emptied on `stream`.  Returns MAC_ERR_INVALID_ARG,
+ * MAC_ERR_UNSUPPORTED, MAC_ERR_CAPACITY (a length beyond capacity) or
+ * MAC_ERR_DEVICE.
+ */
+mac_status mac_init(const mac_config* cfg, void* ring, void* workspace,
+                    int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                    void* stream, mac_ctx** out);
+
+/*
+ * Append one token per sequence (abstract: "each token re-reads an
+ * ever-growing KV cache"): k_new, v_new are device [batch][Hkv][d] in the
+ * config dtype, already rotated.  Stored at position seq_lens_dev[b], which
+ * is then incremented.  page_table: device int32
+ * [batch][max_pages_per_seq] for a paged cache, NULL otherwise.  Returns
+ * MAC_ERR_CAPACITY if any sequence is full (checked on the host mirror).
+ */
+mac_status mac_append_kv(mac_ctx* ctx, void* k_cache, void* v_cache,
+                         const int32_t* page_table, const void* k_new,
+                         const void* v_new, void* stream);
+
+/*
+ * Bulk append for one sequence: k_src, v_src are device [Hkv][count][d]
+ * (natural layout, rotated keys), stored at positions
+ * [seq_lens_dev[seq], +count); seq_lens_dev[seq] grows by count.
+ */
+mac_status mac_prefill_kv(mac_ctx* ctx, void* k_cache, void* v_cache,
+                          const int32_t* page_table, int32_t seq,
+                          const void* k_src, const void* v_src, int32_t count,
+                          void* stream);
+
+/*
+ * Gather positions [start, start+count) of sequence seq back to natural
+ * layout: k_dst, v_dst device [Hkv][count][d].  Caller guarantees the range
+ * was written.  For checkpoints and tests.
+ */
+mac_status mac_read_kv(mac_ctx* ctx, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, int32_t seq, int32_t start,
+                       int32_t count, void* k_dst, void* v_dst, void* stream);
+
+/*
+ * One MAC decode step for every sequence (abstract: match, amend, complete).
+ *   q_pre          device [batch][Hq][d] config dtype: pre-RoPE queries of
+ *                  the token at position seq_lens_dev[b]-1.
+ *   k/v_cache      the caches written by mac_append_kv / mac_prefill_kv.
+ *   page_table     device, paged caches only (else NULL).
+ *   out            device fp32 [batch][Hq][d]: attention output.
+ *   match_ctx_out  device int32 [batch][Hq] or NULL: context length of the
+ *                  matched entry on a hit, -1 on a miss.
+ *   dist_out       device fp32 [batch][Hq] or NULL: L2 distance to the best
+ *                  candidate entry (hit or not); +inf if there is none.
+ * Requires seq_lens >= 1 for every sequence (checked on the host mirror).
+ */
+mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, float* out,
+                           int32_t* match_ctx_out, float* dist_out,
+                           void* stream);
+
+/*
+ * Push entries into the rings directly (e.g. states computed at prefill so
+ * that the first decode steps can match).  Device arrays indexed [b][h]:
+ * q_pre [batch][Hq][d] dtype, o fp32 [batch][Hq][d] (normalized), m, l fp32
+ * [batch][Hq] (natural log base), prefix_end, ctx_len int32 [batch][Hq].
+ * mask uint8 [batch][Hq] or NULL (= push for every head).  The oldest entry
+ * beyond W is evicted.  Entries with prefix_end outside [0, p_new] of a
+ * later step are never matched by that step.
+ */
+mac_status mac_query_cache_push(mac_ctx* ctx, const void* q_pre,
+                                const float* o, const float* m, const float* l,
+                                const int32_t* prefix_end,
+                                const int32_t* ctx_len, const uint8_t* mask,
+                                void* stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, each mac_decode_step
+ * records a pair of HIP events around its split-K attention launch on the
+ * step's stream (at most 65536 pairs are kept).  mac_profile_read waits for
+ * the recorded events, returns the summed milliseconds and the number of
+ * launches timed, and clears the record.
+ */
+mac_status mac_profile_enable(mac_ctx* ctx, int enable);
+mac_status mac_profile_read(mac_ctx* ctx, double* ms_total, int64_t* launches);
+
+/* Release the host context (never frees caller memory). NULL is a no-op. */
+mac_status mac_destroy(mac_ctx* ctx);
+
+/* Last error message of the calling thread ("" if none). */
+const char* mac_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMAC_MAC_H */

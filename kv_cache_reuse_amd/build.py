@@ -1,0 +1,40 @@
+"""Build libmac.so in-tree for gfx950 with hipcc.
+
+    python -m kv_cache_reuse_amd.build
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCES = ["csrc/kernels.hip", "csrc/mac_api.hip"]
+OUT = os.path.join(HERE, "libmac.so")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    # keep the compiler from forming packed fp32 ops (see the design notes)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = OUT + ".tmp"
+    cmd = [hipcc, *FLAGS, "-o", tmp, *[os.path.join(HERE, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
+    if r.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError(f"hipcc failed with status {r.returncode}")
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,424 @@
+// libmac C ABI: argument checks, buffer carving, host length mirror and
+// launch orchestration.  The declarations and the contract are in
+// include/mac.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/mac.h"
+#include "mac_dev.h"
+#include "mac_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mac_status fail(mac_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mac_status fail(mac_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mac_status ok() {
+  g_last_error.clear();
+  return MAC_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  // ring
+  size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
+  // workspace
+  size_t w_plan, w_qfrag, w_po, w_pml, ws_bytes;
+  int slices;
+  int64_t capacity;     // keys per sequence
+  int tiles_per_seq;    // contiguous cache
+};
+
+int elem_size(int dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
+
+mac_status check_config(const mac_config* c) {
+  if (!c) return fail(MAC_ERR_INVALID_ARG, "config is NULL");
+  if (c->batch < 1) return fail(MAC_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", c->batch);
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(MAC_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(MAC_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > mac::kMaxGroup)
+    return fail(MAC_ERR_UNSUPPORTED, "query heads per KV head must be <= %d (got %d)", mac::kMaxGroup,
+                c->n_q_heads / c->n_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(MAC_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->dtype != MAC_DTYPE_F32 && c->dtype != MAC_DTYPE_BF16)
+    return fail(MAC_ERR_UNSUPPORTED, "dtype must be MAC_DTYPE_F32 or MAC_DTYPE_BF16 (got %d)", c->dtype);
+  if (c->window < 0) return fail(MAC_ERR_INVALID_ARG, "window must be >= 0 (got %d)", c->window);
+  if (c->band < 0) return fail(MAC_ERR_INVALID_ARG, "band must be >= 0 (got %d)", c->band);
+  if (!(c->tau >= 0.f)) return fail(MAC_ERR_INVALID_ARG, "tau must be >= 0 (got %g)", (double)c->tau);
+  if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
+    return fail(MAC_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (c->max_slices != 0 && c->max_slices < 2)
+    return fail(MAC_ERR_INVALID_ARG, "max_slices must be 0 (default) or >= 2 (got %d)", c->max_slices);
+  if (c->page_size == 0) {
+    if (c->max_context < 1)
+      return fail(MAC_ERR_INVALID_ARG, "max_context must be >= 1 (got %d)", c->max_context);
+  } else if (c->page_size == mac::kTile) {
+    if (c->max_pages_per_seq < 1 || c->n_pages < 1)
+      return fail(MAC_ERR_INVALID_ARG, "paged cache needs max_pages_per_seq >= 1 and n_pages >= 1");
+    if ((int64_t)c->max_pages_per_seq * mac::kTile > INT32_MAX)
+      return fail(MAC_ERR_INVALID_ARG, "max_pages_per_seq too large");
+  } else {
+    return fail(MAC_ERR_UNSUPPORTED, "page_size must be 0 (contiguous) or 16 (got %d)", c->page_size);
+  }
+  return MAC_OK;
+}
+
+Layout layout(const mac_config* c) {
+  Layout L{};
+  const size_t bh = (size_t)c->batch * c->n_q_heads;
+  const size_t slots = (size_t)c->window + 1;
+  const size_t d = c->head_dim;
+  const size_t es = elem_size(c->dtype);
+  size_t off = 0;
+  L.r_count = off; off = align256(off + bh * 4);
+  L.r_q = off;     off = align256(off + bh * slots * d * es);
+  L.r_o = off;     off = align256(off + bh * slots * d * 4);
+  L.r_ml = off;    off = align256(off + bh * slots * 2 * 4);
+  L.r_pn = off;    off = align256(off + bh * slots * 2 * 4);
+  L.ring_bytes = off;
+
+  L.capacity = c->page_size ? (int64_t)c->max_pages_per_seq * mac::kTile : (int64_t)c->max_context;
+  L.tiles_per_seq = c->page_size ? 0 : mac::ceil_div(c->max_context, mac::kTile);
+  const int groups = c->batch * c->n_kv_heads;
+  int S = c->max_slices;
+  if (S == 0) {
+    // about four 256-thread workgroups per compute unit on a 256-CU part,
+    // never more slices than the longest context can fill
+    S = mac::ceil_div(1024, groups);
+    const int cap = (int)((L.capacity + mac::kSliceMin - 1) / mac::kSliceMin) + 1;
+    if (S > cap) S = cap;
+    if (S < 2) S = 2;
+  }
+  L.slices = S;
+  const size_t G = c->n_q_heads / c->n_kv_heads;
+  off = 0;
+  L.w_plan = off;  off = align256(off + bh * sizeof(mac::HeadPlan));
+  L.w_qfrag = off; off = align256(off + bh * d * 4);
+  L.w_po = off;    off = align256(off + (size_t)groups * S * G * d * 4);
+  L.w_pml = off;   off = align256(off + (size_t)groups * S * G * 2 * 4);
+  L.ws_bytes = off;
+  return L;
+}
+
+}  // namespace
+
+struct mac_ctx {
+  mac_config cfg;
+  Layout L;
+  char* ring;
+  char* ws;
+  int32_t* seq_lens_dev;
+  std::vector<int64_t> mirror;
+  bool poisoned = false;
+  bool profiling = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t ev_used = 0;
+
+  mac::RingView ring_view() const {
+    mac::RingView R;
+    R.count = reinterpret_cast<int32_t*>(ring + L.r_count);
+    R.q = ring + L.r_q;
+    R.o = reinterpret_cast<float*>(ring + L.r_o);
+    R.ml = reinterpret_cast<float*>(ring + L.r_ml);
+    R.pn = reinterpret_cast<int32_t*>(ring + L.r_pn);
+    R.slots = cfg.window + 1;
+    R.window = cfg.window;
+    return R;
+  }
+  mac::KvGeom geom() const {
+    mac::KvGeom g;
+    g.hkv = cfg.n_kv_heads;
+    g.d = cfg.head_dim;
+    g.tiles_per_seq = L.tiles_per_seq;
+    g.paged = cfg.page_size ? 1 : 0;
+    g.max_pages = cfg.max_pages_per_seq;
+    return g;
+  }
+};
+
+namespace {
+
+mac_status check_ctx(mac_ctx* ctx) {
+  if (!ctx) return fail(MAC_ERR_INVALID_ARG, "context is NULL");
+  if (ctx->poisoned) return fail(MAC_ERR_STATE, "context unusable after an earlier device error");
+  return MAC_OK;
+}
+
+mac_status device_fail(mac_ctx* ctx, hipError_t e, const char* what) {
+  if (ctx) ctx->poisoned = true;
+  return fail(MAC_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+mac_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(MAC_ERR_INVALID_ARG, "%s is NULL", name) : MAC_OK;
+  if (!aligned16(p)) return fail(MAC_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MAC_OK;
+}
+
+mac_status check_kv(mac_ctx* ctx, const void* k, const void* v, const int32_t* pt) {
+  mac_status s;
+  if ((s = check_ptr(k, "k_cache"))) return s;
+  if ((s = check_ptr(v, "v_cache"))) return s;
+  if (ctx->cfg.page_size) {
+    if (!pt) return fail(MAC_ERR_INVALID_ARG, "page_table is required for a paged cache");
+    if ((s = check_ptr(pt, "page_table"))) return s;
+  } else if (pt) {
+    return fail(MAC_ERR_INVALID_ARG, "page_table given for a contiguous cache");
+  }
+  return MAC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mac_kv_cache_bytes(const mac_config* cfg) {
+  if (check_config(cfg)) return 0;
+  const size_t tile = (size_t)mac::kTile * cfg->head_dim * elem_size(cfg->dtype);
+  if (cfg->page_size) return (size_t)cfg->n_pages * cfg->n_kv_heads * tile;
+  return (size_t)cfg->batch * cfg->n_kv_heads * mac::ceil_div(cfg->max_context, mac::kTile) * tile;
+}
+
+size_t mac_ring_bytes(const mac_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return layout(cfg).ring_bytes;
+}
+
+size_t mac_workspace_bytes(const mac_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return layout(cfg).ws_bytes;
+}
+
+mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t* seq_lens_dev,
+                    const int32_t* seq_lens_host, void* stream, mac_ctx** out) {
+  mac_status s;
+  if (!out) return fail(MAC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if ((s = check_config(cfg))) return s;
+  if ((s = check_ptr(ring, "ring"))) return s;
+  if ((s = check_ptr(workspace, "workspace"))) return s;
+  if ((s = check_ptr(seq_lens_dev, "seq_lens_dev"))) return s;
+  if (!seq_lens_host) return fail(MAC_ERR_INVALID_ARG, "seq_lens_host is NULL");
+  const Layout L = layout(cfg);
+  for (int b = 0; b < cfg->batch; ++b)
+    if (seq_lens_host[b] < 0 || seq_lens_host[b] > L.capacity)
+      return fail(MAC_ERR_CAPACITY, "seq_lens_host[%d] = %d outside [0, %lld]", b, seq_lens_host[b],
+                  (long long)L.capacity);
+  mac_ctx* ctx = new (std::nothrow) mac_ctx;
+  if (!ctx) return fail(MAC_ERR_INVALID_ARG, "out of host memory");
+  ctx->cfg = *cfg;
+  ctx->L = L;
+  ctx->ring = static_cast<char*>(ring);
+  ctx->ws = static_cast<char*>(workspace);
+  ctx->seq_lens_dev = seq_lens_dev;
+  ctx->mirror.assign(seq_lens_host, seq_lens_host + cfg->batch);
+  hipError_t e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
+                                      cfg->batch * cfg->n_q_heads, 0,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete ctx;
+    return device_fail(nullptr, e, "mac_init: clearing the ring");
+  }
+  *out = ctx;
+  return ok();
+}
+
+mac_status mac_append_kv(mac_ctx* ctx, void* k_cache, void* v_cache, const int32_t* page_table,
+                         const void* k_new, const void* v_new, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
+  if ((s = check_ptr(k_new, "k_new"))) return s;
+  if ((s = check_ptr(v_new, "v_new"))) return s;
+  for (int b = 0; b < ctx->cfg.batch; ++b)
+    if (ctx->mirror[b] + 1 > ctx->L.capacity)
+      return fail(MAC_ERR_CAPACITY, "sequence %d is full (%lld keys)", b, (long long)ctx->mirror[b]);
+  hipError_t e = mac::launch_append(k_cache, v_cache, page_table, k_new, v_new, ctx->seq_lens_dev,
+                                    ctx->geom(), ctx->cfg.batch, ctx->cfg.dtype,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_append_kv");
+  for (auto& n : ctx->mirror) ++n;
+  return ok();
+}
+
+mac_status mac_prefill_kv(mac_ctx* ctx, void* k_cache, void* v_cache, const int32_t* page_table,
+                          int32_t seq, const void* k_src, const void* v_src, int32_t count,
+                          void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
+  if (seq < 0 || seq >= ctx->cfg.batch)
+    return fail(MAC_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, ctx->cfg.batch);
+  if (count < 0) return fail(MAC_ERR_INVALID_ARG, "count must be >= 0 (got %d)", count);
+  if (count == 0) return ok();
+  if ((s = check_ptr(k_src, "k_src"))) return s;
+  if ((s = check_ptr(v_src, "v_src"))) return s;
+  if (ctx->mirror[seq] + count > ctx->L.capacity)
+    return fail(MAC_ERR_CAPACITY, "sequence %d: %lld + %d keys exceed capacity %lld", seq,
+                (long long)ctx->mirror[seq], count, (long long)ctx->L.capacity);
+  hipError_t e = mac::launch_prefill(k_cache, v_cache, page_table, k_src, v_src, ctx->seq_lens_dev,
+                                     seq, count, ctx->geom(), ctx->cfg.dtype,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_prefill_kv");
+  ctx->mirror[seq] += count;
+  return ok();
+}
+
+mac_status mac_read_kv(mac_ctx* ctx, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, int32_t seq, int32_t start, int32_t count,
+                       void* k_dst, void* v_dst, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
+  if (seq < 0 || seq >= ctx->cfg.batch)
+    return fail(MAC_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, ctx->cfg.batch);
+  if (start < 0 || count < 0 || (int64_t)start + count > ctx->mirror[seq])
+    return fail(MAC_ERR_INVALID_ARG, "range [%d, %d + %d) outside the %lld stored keys", start, start,
+                count, (long long)ctx->mirror[seq]);
+  if (count == 0) return ok();
+  if ((s = check_ptr(k_dst, "k_dst"))) return s;
+  if ((s = check_ptr(v_dst, "v_dst"))) return s;
+  hipError_t e = mac::launch_read(k_cache, v_cache, page_table, k_dst, v_dst, seq, start, count,
+                                  ctx->geom(), ctx->cfg.dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_read_kv");
+  return ok();
+}
+
+mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, float* out,
+                           int32_t* match_ctx_out, float* dist_out, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
+  if ((s = check_ptr(q_pre, "q_pre"))) return s;
+  if ((s = check_ptr(out, "out"))) return s;
+  if ((s = check_ptr(match_ctx_out, "match_ctx_out", false))) return s;
+  if ((s = check_ptr(dist_out, "dist_out", false))) return s;
+  for (int b = 0; b < ctx->cfg.batch; ++b)
+    if (ctx->mirror[b] < 1)
+      return fail(MAC_ERR_INVALID_ARG, "sequence %d has no keys: append before decoding", b);
+
+  const mac_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  mac::StepArgs a;
+  a.q_pre = q_pre;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.seq_lens = ctx->seq_lens_dev;
+  a.out = out;
+  a.match_ctx_out = match_ctx_out;
+  a.dist_out = dist_out;
+  a.plan = reinterpret_cast<mac::HeadPlan*>(ctx->ws + L.w_plan);
+  a.qfrag = ctx->ws + L.w_qfrag;
+  a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
+  a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
+  a.part.S = L.slices;
+  a.ring = ctx->ring_view();
+  a.geom = ctx->geom();
+  a.batch = c.batch;
+  a.hq = c.n_q_heads;
+  a.hkv = c.n_kv_heads;
+  a.group = c.n_q_heads / c.n_kv_heads;
+  a.band = c.band;
+  a.tau2 = static_cast<float>((double)c.tau * (double)c.tau);
+  a.theta = c.rope_theta;
+
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (ctx->profiling && ctx->ev_used < 65536) {
+    if (ctx->ev_used == ctx->events.size()) {
+      hipEvent_t x, y;
+      hipError_t e = hipEventCreate(&x);
+      if (e == hipSuccess) e = hipEventCreate(&y);
+      if (e != hipSuccess) return device_fail(ctx, e, "mac_decode_step: creating timing events");
+      ctx->events.emplace_back(x, y);
+    }
+    e0 = ctx->events[ctx->ev_used].first;
+    e1 = ctx->events[ctx->ev_used].second;
+    ++ctx->ev_used;
+  }
+  hipError_t e = mac::launch_step(a, c.dtype, c.head_dim, c.page_size ? 1 : 0,
+                                  static_cast<hipStream_t>(stream), e0, e1);
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_decode_step");
+  return ok();
+}
+
+mac_status mac_query_cache_push(mac_ctx* ctx, const void* q_pre, const float* o, const float* m,
+                                const float* l, const int32_t* prefix_end, const int32_t* ctx_len,
+                                const uint8_t* mask, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if ((s = check_ptr(q_pre, "q_pre"))) return s;
+  if ((s = check_ptr(o, "o"))) return s;
+  if (!m || !l || !prefix_end || !ctx_len)
+    return fail(MAC_ERR_INVALID_ARG, "m, l, prefix_end and ctx_len are required");
+  hipError_t e = mac::launch_push(ctx->ring_view(), ctx->cfg.batch, ctx->cfg.n_q_heads,
+                                  ctx->cfg.head_dim, ctx->cfg.dtype, q_pre, o, m, l, prefix_end,
+                                  ctx_len, mask, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_query_cache_push");
+  return ok();
+}
+
+mac_status mac_profile_enable(mac_ctx* ctx, int enable) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  ctx->profiling = enable != 0;
+  return ok();
+}
+
+mac_status mac_profile_read(mac_ctx* ctx, double* ms_total, int64_t* launches) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if (!ms_total || !launches) return fail(MAC_ERR_INVALID_ARG, "ms_total and launches are required");
+  double tot = 0.0;
+  for (size_t i = 0; i < ctx->ev_used; ++i) {
+    hipError_t e = hipEventSynchronize(ctx->events[i].second);
+    if (e != hipSuccess) return device_fail(ctx, e, "mac_profile_read");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ctx->events[i].first, ctx->events[i].second);
+    if (e != hipSuccess) return device_fail(ctx, e, "mac_profile_read");
+    tot += ms;
+  }
+  *ms_total = tot;
+  *launches = (int64_t)ctx->ev_used;
+  ctx->ev_used = 0;
+  return ok();
+}
+
+mac_status mac_destroy(mac_ctx* ctx) {
+  if (!ctx) return ok();
+  for (auto& p : ctx->events) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  delete ctx;
+  return ok();
+}
+
+const char* mac_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Device-side definitions shared by the libmac kernels (gfx950).
+//
+// Contents: bf16 conversion, the 16-token KV tile permutation, the ring and
+// workspace layouts, and the split-K plan that the attention and merge
+// kernels derive identically from the match results.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mac {
+
+constexpr int kTile = 16;        // tokens per KV tile (= page size when paged)
+constexpr int kSliceMin = 256;   // fewest keys a split-K slice is given
+constexpr int kMaxGroup = 16;    // query heads per KV head: the MFMA N width
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round to nearest, ties to even (IEEE 754 binary32 -> bfloat16); NaN stays
+// a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float to_f(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static float to_f(uint16_t x) { return bf16_to_f32(x); }
+};
+
+// ---------------------------------------------------------- KV tiles ----
+// A tile holds 16 tokens x D elements of one (sequence, KV head).  Its bytes
+// are split into 1 KiB blocks; lane l of a wave reads bytes [16 l, 16 l + 16)
+// of block j with one 128-bit load.  Let E = 16 / sizeof(T) be the elements
+// of one such 16-byte piece, lg = l / 16 and c = l % 16.
+//
+// Keys: lane (lg, c) of block j holds token c, dims [E (4 j + lg), +E): the
+//   A operand (rows = tokens, k = dims) of the QK^T matrix-core product.
+// Values: lane (lg, c) of block i holds tokens 4 lg .. 4 lg + 3 of dim c of
+//   E/4 consecutive 16-dim column tiles (ct = (E/4) i + th): the A operand
+//   (rows = dims, k = tokens) of the O^T = V^T P^T product, whose k index
+//   (tokens 4 lg + r) matches the row order of the QK^T accumulator.
+template <typename T>
+__host__ __device__ __forceinline__ int k_tile_offset(int tok, int dim) {
+  constexpr int E = 16 / sizeof(T);
+  const int piece = dim / E, e = dim % E;
+  const int j = piece / 4, lg = piece % 4;
+  return j * (64 * E) + (lg * 16 + tok) * E + e;
+}
+
+template <typename T>
+__host__ __device__ __forceinline__ int v_tile_offset(int tok, int dim) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int TP = E / 4;               // column tiles per 16-byte piece
+  const int ct = dim / 16, c = dim % 16;
+  const int i = ct / TP, th = ct % TP;
+  const int lg = tok / 4, r = tok % 4;
+  return i * (64 * E) + (lg * 16 + c) * E + th * 4 + r;
+}
+
+struct KvGeom {
+  int hkv, d;
+  int tiles_per_seq;     // contiguous: ceil(max_context / 16)
+  int paged;             // 1: tile t of sequence b is page_table[b*mp + t]
+  int max_pages;         // paged: page-table columns
+};
+
+// Element offset of the start of tile t of (b, g).
+__device__ __forceinline__ int64_t tile_base(const KvGeom& g, const int32_t* pt,
+                                             int b, int kvh, int t) {
+  const int64_t tile_elems = int64_t(kTile) * g.d;
+  if (g.paged) {
+    const int64_t page = pt[int64_t(b) * g.max_pages + t];
+    return (page * g.hkv + kvh) * tile_elems;
+  }
+  return ((int64_t(b) * g.hkv + kvh) * g.tiles_per_seq + t) * tile_elems;
+}
+
+// --------------------------------------------------------------- ring ----
+// Per (b, h): a push counter and W + 1 slots.  Slot of the k-th most recent
+// entry (k = 0 newest) is (count - 1 - k) mod (W + 1); a push writes slot
+// count mod (W + 1), which is never one of the W entries a step can match.
+struct RingView {
+  int32_t* count;   // [batch*Hq]
+  void* q;          // [batch*Hq][W+1][D] dtype
+  float* o;         // [batch*Hq][W+1][D]
+  float* ml;        // [batch*Hq][W+1][2]  (m natural log base, l)
+  int32_t* pn;      // [batch*Hq][W+1][2]  (prefix end p, context length n)
+  int slots;        // W + 1
+  int window;       // W
+};
+
+// ---------------------------------------------------------- workspace ----
+struct HeadPlan {   // written by the match kernel, one per (b, h)
+  int32_t hit;      // 1 on a hit
+  int32_t slot;     // ring slot of the matched entry (valid on a hit)
+  int32_t s;        // start of the fresh key range
+  int32_t pad;
+};
+
+// Split-K plan of one KV group: fresh keys [lo, hi) split at mid = p_new
+// into n_pre slices over [lo, mid) and n_post slices over [mid, hi).
+// Interior boundaries fall on 16-token tile edges.
+struct Plan {
+  int lo, mid, hi, n_pre, n_post;
+};
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__host__ __device__ __forceinline__ Plan make_plan(int lo, int n, int band, int max_slices) {
+  Plan p;
+  p.hi = n;
+  p.mid = n - band > 0 ? n - band : 0;
+  p.lo = lo < p.mid ? lo : p.mid;
+  const int lpre = p.mid - p.lo, lpost = p.hi - p.mid;
+  const int post_cap = max_slices / 2 > 1 ? max_slices / 2 : 1;
+  p.n_post = lpost > 0 ? min(ceil_div(lpost, kSliceMin), post_cap) : 0;
+  const int pre_cap = max_slices - p.n_post;
+  p.n_pre = lpre > 0 ? min(ceil_div(lpre, kSliceMin), pre_cap) : 0;
+  return p;
+}
+
+__host__ __device__ __forceinline__ int split_bound(int a, int e, int n, int i) {
+  if (i <= 0) return a;
+  if (i >= n) return e;
+  int x = a + static_cast<int>((int64_t(e - a) * i) / n);
+  x &= ~(kTile - 1);
+  return x > a ? x : a;
+}
+
+// Key range [*a, *e) of slice i of a plan (i < n_pre + n_post).
+__host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* a, int* e) {
+  if (i < p.n_pre) {
+    *a = split_bound(p.lo, p.mid, p.n_pre, i);
+    *e = split_bound(p.lo, p.mid, p.n_pre, i + 1);
+  } else {
+    const int k = i - p.n_pre;
+    *a = split_bound(p.mid, p.hi, p.n_post, k);
+    *e = split_bound(p.mid, p.hi, p.n_post, k + 1);
+  }
+}
+
+// Partial states: o unnormalized, m in log2 units of the scaled score.
+struct PartialView {
+  float* o;    // [groups][S][G][D]
+  float* ml;   // [groups][S][G][2]
+  int S;
+};
+
+struct StepArgs {
+  const void* q_pre;        // [batch][Hq][D] dtype
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;  // [batch]
+  float* out;               // [batch][Hq][D]
+  int32_t* match_ctx_out;   // nullable
+  float* dist_out;          // nullable
+  HeadPlan* plan;           // [batch*Hq]
+  void* qfrag;              // [batch*Hq][D] hi bf16 then [batch*Hq][D] lo bf16; or fp32
+  PartialView part;
+  RingView ring;
+  KvGeom geom;
+  int batch, hq, hkv, group, band;
+  float tau2;               // tau^2 rounded to fp32
+  double theta;
+};
+
+}  // namespace mac

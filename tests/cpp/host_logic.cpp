@@ -1,0 +1,102 @@
+// Host checks of libmac's integer logic, compiled from the library's own
+// header: the KV tile permutations are bijections onto the tile, and the
+// split-K plan partitions the fresh range [lo, n) into slices that never
+// straddle p_new, with every slice non-empty and at most max_slices of them.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "../../kv_cache_reuse_amd/csrc/mac_dev.h"
+
+static int fails = 0;
+#define CHECK(c, ...)                         \
+  do {                                        \
+    if (!(c)) {                               \
+      if (fails < 20) {                       \
+        std::printf("FAIL %s: ", #c);         \
+        std::printf(__VA_ARGS__);             \
+        std::printf("\n");                    \
+      }                                       \
+      ++fails;                                \
+    }                                         \
+  } while (0)
+
+template <typename T>
+void check_tiles(int D) {
+  std::vector<int> seen_k(16 * D, 0), seen_v(16 * D, 0);
+  for (int tok = 0; tok < 16; ++tok)
+    for (int d = 0; d < D; ++d) {
+      int ko = mac::k_tile_offset<T>(tok, d), vo = mac::v_tile_offset<T>(tok, d);
+      CHECK(ko >= 0 && ko < 16 * D, "k offset %d (tok %d dim %d D %d)", ko, tok, d, D);
+      CHECK(vo >= 0 && vo < 16 * D, "v offset %d (tok %d dim %d D %d)", vo, tok, d, D);
+      if (ko >= 0 && ko < 16 * D) seen_k[ko]++;
+      if (vo >= 0 && vo < 16 * D) seen_v[vo]++;
+    }
+  for (int i = 0; i < 16 * D; ++i) {
+    CHECK(seen_k[i] == 1, "k slot %d hit %d times (D %d)", i, seen_k[i], D);
+    CHECK(seen_v[i] == 1, "v slot %d hit %d times (D %d)", i, seen_v[i], D);
+  }
+  // lane view: lane l of 1 KiB block j reads elements [64 E j + E l, +E)
+  constexpr int E = 16 / sizeof(T);
+  for (int tok = 0; tok < 16; ++tok)
+    for (int d = 0; d < D; ++d) {
+      int ko = mac::k_tile_offset<T>(tok, d);
+      int j = ko / (64 * E), lane = (ko % (64 * E)) / E, e = ko % E;
+      CHECK(lane % 16 == tok, "k lane %d holds token %d", lane, tok);
+      CHECK(d == E * (4 * j + lane / 16) + e, "k lane %d block %d elem %d holds dim %d", lane, j, e, d);
+      int vo = mac::v_tile_offset<T>(tok, d);
+      int i = vo / (64 * E), vl = (vo % (64 * E)) / E, ve = vo % E;
+      CHECK(vl % 16 == d % 16, "v lane %d holds dim %d", vl, d);
+      CHECK(tok == 4 * (vl / 16) + ve % 4, "v lane %d elem %d holds token %d", vl, ve, tok);
+      CHECK(d / 16 == (E / 4) * i + ve / 4, "v block %d elem %d holds column tile of dim %d", i, ve, d);
+    }
+}
+
+void check_plan(int lo, int n, int band, int S) {
+  mac::Plan p = mac::make_plan(lo, n, band, S);
+  const int mid = n - band > 0 ? n - band : 0;
+  CHECK(p.mid == mid && p.hi == n, "mid/hi");
+  CHECK(p.n_pre + p.n_post <= S, "too many slices %d + %d > %d", p.n_pre, p.n_post, S);
+  CHECK((p.lo < p.mid) == (p.n_pre > 0), "pre slices %d for [%d, %d)", p.n_pre, p.lo, p.mid);
+  CHECK((p.mid < p.hi) == (p.n_post > 0), "post slices %d for [%d, %d)", p.n_post, p.mid, p.hi);
+  int cur = p.lo;
+  for (int i = 0; i < p.n_pre + p.n_post; ++i) {
+    int a, e;
+    mac::slice_range(p, i, &a, &e);
+    if (i == p.n_pre) CHECK(cur == p.mid, "pre slices end at %d, not mid %d", cur, p.mid);
+    CHECK(a == cur, "slice %d starts at %d, expected %d (lo %d n %d B %d S %d)", i, a, cur, lo, n, band, S);
+    CHECK(e > a, "slice %d empty [%d, %d) (lo %d n %d B %d S %d)", i, a, e, lo, n, band, S);
+    if (i < p.n_pre) CHECK(e <= p.mid, "pre slice passes mid");
+    else CHECK(a >= p.mid, "post slice before mid");
+    bool interior_end = (i != p.n_pre - 1) && (i != p.n_pre + p.n_post - 1);
+    if (interior_end) CHECK(e % 16 == 0, "interior bound %d not on a tile edge", e);
+    cur = e;
+  }
+  CHECK(cur == (p.n_post ? p.hi : p.mid), "slices end at %d", cur);
+}
+
+int main() {
+  check_tiles<uint16_t>(64);
+  check_tiles<uint16_t>(128);
+  check_tiles<float>(64);
+  check_tiles<float>(128);
+  std::mt19937 rng(123);
+  const int Ss[] = {2, 3, 8, 16, 34, 128, 1024};
+  for (int it = 0; it < 200000; ++it) {
+    int n = 1 + rng() % (it % 3 == 0 ? 300 : 200000);
+    int band = rng() % 4 == 0 ? 0 : rng() % 600;
+    int mid = n - band > 0 ? n - band : 0;
+    int lo = rng() % 2 ? 0 : (int)(rng() % (mid + 1));
+    int S = Ss[rng() % 7];
+    check_plan(lo, n, band, S);
+  }
+  check_plan(0, 131072 + 512, 256, 128);
+  check_plan(131072 + 300 - 256 - 1, 131072 + 300, 256, 128);
+  if (fails) {
+    std::printf("%d failures\n", fails);
+    return 1;
+  }
+  std::printf("OK\n");
+  return 0;
+}

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point
+include/mac.h declares, and rejects bad arguments before any HIP call.  Also
+compiles and runs the host check of the kernels' integer logic."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    import kv_cache_reuse_amd.binding as B
+    return B
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "mac.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(mac_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(B.library(), n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def valid_cfg(B, **kw):
+    c = B.MacConfig()
+    c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim = 1, 32, 8, 128
+    c.dtype = B.MAC_DTYPE_BF16
+    c.max_context, c.window, c.band, c.tau, c.rope_theta = 4096, 32, 256, 5.0, 5e5
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+BAD = [
+    (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(n_q_heads=30), 1),
+    (dict(n_q_heads=8 * 17), 2), (dict(head_dim=96), 2), (dict(dtype=7), 2),
+    (dict(window=-1), 1), (dict(band=-3), 1), (dict(tau=-1.0), 1),
+    (dict(tau=float("nan")), 1), (dict(rope_theta=0.0), 1),
+    (dict(rope_theta=float("inf")), 1), (dict(max_slices=1), 1),
+    (dict(max_context=0), 1), (dict(page_size=8), 2),
+    (dict(page_size=16, max_pages_per_seq=0, n_pages=4), 1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BAD)))
+def test_bad_configs_are_rejected(B, i):
+    kw, status = BAD[i]
+    cfg = valid_cfg(B, **kw)
+    assert B.mac_ring_bytes(cfg) == 0
+    assert B.mac_workspace_bytes(cfg) == 0
+    assert B.mac_kv_cache_bytes(cfg) == 0
+    out = ctypes.c_void_p()
+    host = (ctypes.c_int32 * cfg.batch if cfg.batch > 0 else ctypes.c_int32 * 1)()
+    st = B.library().mac_init(ctypes.byref(cfg), 0x10000, 0x20000, 0x30000,
+                              ctypes.cast(host, ctypes.c_void_p), None, ctypes.byref(out))
+    assert st == status, B.mac_last_error()
+    assert out.value is None
+    assert B.mac_last_error()
+
+
+def test_sizes_of_a_valid_config(B):
+    cfg = valid_cfg(B)
+    kv = B.mac_kv_cache_bytes(cfg)
+    assert kv == 8 * (4096 // 16) * 16 * 128 * 2
+    ring = B.mac_ring_bytes(cfg)
+    assert ring >= 32 * 33 * (128 * 2 + 128 * 4 + 16)
+    assert B.mac_workspace_bytes(cfg) > 0
+    paged = valid_cfg(B, page_size=16, max_pages_per_seq=300, n_pages=1000)
+    assert B.mac_kv_cache_bytes(paged) == 1000 * 8 * 16 * 128 * 2
+
+
+def test_pointer_and_capacity_errors_come_before_device_calls(B):
+    lib = B.library()
+    cfg = valid_cfg(B)
+    out = ctypes.c_void_p()
+    host = (ctypes.c_int32 * 1)(0)
+    hp = ctypes.cast(host, ctypes.c_void_p)
+    assert lib.mac_init(ctypes.byref(cfg), None, 0x20000, 0x30000, hp, None, ctypes.byref(out)) == 1
+    assert "ring" in B.mac_last_error()
+    assert lib.mac_init(ctypes.byref(cfg), 0x10008, 0x20000, 0x30000, hp, None, ctypes.byref(out)) == 1
+    assert "aligned" in B.mac_last_error()
+    assert lib.mac_init(ctypes.byref(cfg), 0x10000, 0x20000, 0x30000, None, None, ctypes.byref(out)) == 1
+    host[0] = 4097
+    assert lib.mac_init(ctypes.byref(cfg), 0x10000, 0x20000, 0x30000, hp, None, ctypes.byref(out)) == 3
+    host[0] = -1
+    assert lib.mac_init(ctypes.byref(cfg), 0x10000, 0x20000, 0x30000, hp, None, ctypes.byref(out)) == 3
+    assert lib.mac_init(ctypes.byref(cfg), 0x10000, 0x20000, 0x30000, hp, None, None) == 1
+
+
+def test_null_context_calls(B):
+    lib = B.library()
+    assert lib.mac_append_kv(None, 16, 16, None, 16, 16, None) == 1
+    assert lib.mac_decode_step(None, 16, 16, 16, None, 16, None, None, None) == 1
+    assert lib.mac_prefill_kv(None, 16, 16, None, 0, 16, 16, 1, None) == 1
+    assert lib.mac_read_kv(None, 16, 16, None, 0, 0, 1, 16, 16, None) == 1
+    assert lib.mac_query_cache_push(None, 16, 16, 16, 16, 16, 16, None, None) == 1
+    assert lib.mac_profile_enable(None, 1) == 1
+    assert lib.mac_destroy(None) == 0
+
+
+def test_host_integer_logic(tmp_path):
+    exe = str(tmp_path / "host_logic_test")
+    src = os.path.join(ROOT, "tests", "cpp", "host_logic.cpp")
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O1", "-std=c++17",
+                        "-x", "hip", src, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout[-2000:]

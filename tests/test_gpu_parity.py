@@ -1,0 +1,155 @@
+"""GPU parity of libmac against the fp64 oracle (needs an MI355X).
+
+Small shapes (several 16-token tiles, ragged tails, every KV group) are
+checked on every step; the full-size shapes run in the launch configuration
+the benchmark uses and are checked on sampled KV groups, the oracle
+replaying those groups step by step.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from synth.streams import make_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_harness import OUT_TOL, check_groups, run_gpu, say  # noqa: E402
+
+
+def all_groups(w):
+    return [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+
+
+def assert_report(rep, name, min_hits=1):
+    say(f"[{name}] steps={rep.steps} heads={rep.heads} hits={rep.hits} "
+        f"max_err={rep.max_err:.3e} dist_err={rep.max_dist_err:.2e} "
+        f"borderline={len(rep.borderline)} mismatches={rep.mismatches[:5]}")
+    assert not rep.mismatches, rep.mismatches[:10]
+    assert rep.max_err <= OUT_TOL
+    assert rep.max_dist_err <= 1e-5
+    assert rep.hits >= min_hits
+
+
+SMALL = {
+    "tiny_full": ("tiny", {}),
+    "8b_32k_ragged": ("8b_32k", dict(context=3001, steps=40)),
+    "8b_128k_p05": ("8b_128k", dict(context=5003, steps=48, p_jump=0.5)),
+    "8b_128k_p005": ("8b_128k", dict(context=4099, steps=48, p_jump=0.05)),
+    "paged_b8_small": ("paged_b8", dict(ctx_range=(700, 2300), steps=32)),
+    "70b_small": ("70b_128k", dict(batch=2, context=3333, steps=32)),
+    "band0": ("8b_32k", dict(context=1000, steps=24, band=0, p_jump=0.2)),
+    "window0": ("8b_32k", dict(context=1000, steps=12, window=0)),
+    "band_over_ctx": ("tiny", dict(context=40, steps=40, band=500)),
+    "ctx1": ("tiny", dict(context=1, steps=40, band=8, window=4)),
+    "periodic_tail": ("8b_32k", dict(context=2100, steps=40, period=5, window=8, band=64,
+                                     tau=0.5 * math.sqrt(128))),
+    "d64_bf16": ("8b_32k", dict(head_dim=64, context=1500, steps=24, tau=0.5 * math.sqrt(64))),
+    "d128_f32": ("tiny", dict(head_dim=128, n_q_heads=8, n_kv_heads=2, context=900, steps=24,
+                              tau=0.5 * math.sqrt(128))),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes_every_step(name):
+    base, kw = SMALL[name]
+    w = workload(base, **kw)
+    say(f"[{name}] {w}")
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    min_hits = 0 if (w.window == 0) else 1
+    assert_report(rep, name, min_hits)
+
+
+@pytest.mark.parametrize("name", ["ctx1", "8b_32k_ragged", "paged_b8_small", "d64_bf16"])
+def test_stale_cache_slots_do_not_leak(name):
+    # unwritten cache slots hold NaN; they sit past the end of each sequence
+    # inside its last 16-token tile and must not reach any output
+    base, kw = SMALL[name]
+    w = workload(base, **kw)
+    inp = make_inputs(w, steps=min(w.steps, 20))
+    say(f"[poison:{name}]")
+    gpu = run_gpu(w, inp, poison=True)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"poison:{name}", 0)
+
+
+def test_paged_equals_contiguous_bitwise():
+    w = workload("paged_b8", ctx_range=(500, 1500), steps=16)
+    inp = make_inputs(w)
+    say("[paged_vs_contig] paged")
+    a = run_gpu(w, inp, max_slices=8, paged=True)
+    say("[paged_vs_contig] contiguous")
+    b = run_gpu(w, inp, max_slices=8, paged=False)
+    for t in a.out:
+        np.testing.assert_array_equal(a.out[t], b.out[t])
+        np.testing.assert_array_equal(a.match_n[t], b.match_n[t])
+
+
+def test_runs_are_bitwise_deterministic():
+    w = workload("8b_32k", context=2500, steps=16)
+    inp = make_inputs(w)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for t in a.out:
+        np.testing.assert_array_equal(a.out[t], b.out[t])
+        np.testing.assert_array_equal(a.dist[t], b.dist[t])
+
+
+def test_kv_roundtrip_is_exact():
+    for name, kw in (("8b_32k", dict(context=1000, steps=4)),
+                     ("paged_b8", dict(ctx_range=(300, 800), steps=4)),
+                     ("tiny", dict(context=333, steps=4))):
+        w = workload(name, **kw)
+        inp = make_inputs(w)
+        gpu = run_gpu(w, inp, steps=2)
+        sess = gpu.session
+        for b in range(w.batch):
+            n = int(inp.contexts[b]) + 2
+            k, v = sess.read_kv(b, 0, n)
+            torch.cuda.synchronize()
+            assert torch.equal(k.cpu(), inp.k[b, :, :n])
+            assert torch.equal(v.cpu(), inp.v[b, :, :n])
+
+
+def test_nan_query_poisons_only_its_head():
+    w = workload("8b_32k", context=700, steps=10)
+    inp = make_inputs(w)
+    q = inp.q.clone()
+    q[6, 0, 5, 17] = float("nan")
+    inp.q = q
+    inp.q64 = q.double().numpy()
+    gpu = run_gpu(w, inp)
+    assert np.isnan(gpu.out[6][0, 5]).all()
+    assert gpu.match_n[6][0, 5] == -1
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, "nan_head", 0)
+
+
+# ---------------------------------------------------------------------------
+# full sizes, launch configuration of the benchmark, sampled groups
+# ---------------------------------------------------------------------------
+
+FULL = {
+    "8b_32k": (dict(), None, [(0, 0), (0, 5)]),
+    "8b_128k_p02": (dict(p_jump=0.2), 96, [(0, 3)]),
+    "paged_b8": (dict(), 64, [(2, 1), (7, 6)]),
+    "70b_128k": (dict(), 40, [(1, 2)]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_groups(name):
+    kw, steps, groups = FULL[name]
+    base = name.split("_p0")[0]
+    w = workload(base, **kw)
+    say(f"[full:{name}] generating")
+    inp = make_inputs(w, steps=steps)
+    say(f"[full:{name}] gpu run")
+    gpu = run_gpu(w, inp)
+    say(f"[full:{name}] oracle replay of {groups}")
+    rep = check_groups(w, inp, gpu, groups)
+    assert_report(rep, f"full:{name}")
