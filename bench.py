@@ -1,0 +1,425 @@
+"""Benchmark of the MAC-Attention decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+
+Workload: the Llama-3-8B decode-attention shape at a 131072-key context
+(batch 1, 32 query / 8 KV heads, d = 128, bf16 K/V, W = 32, B = 256,
+tau = 0.5 sqrt(128)).  One step is one pass of the whole hot path for one
+token: append k/v, then match -> split-K attention -> merge (one attention
+layer).  L layer copies (own caches, rings and streams) are visited in turn
+so that consecutive steps do not find the previous step's KV in the 256 MB
+last-level cache.
+
+Printed: one JSON line.  `value` is the effective KV bandwidth of the miss
+path (every step misses: jump probability 1), i.e. algorithmic bytes / time;
+`sweep` holds the hit-rate sweep (jump probability 1, 0.5, 0.2, 0.05) with
+us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
+latency at contexts 8K..128K; `roofline` the split-K kernel's achieved
+bandwidth from HIP events around its launches; `cpu_baseline` the fp64
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = ("decode-attention µs/token + effective KV GB/s (% HBM peak) at 128K, "
+          "hit-rate sweep")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_attn_partial_8b_128k.json")
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", "kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes of one step, from the step's decisions
+# ---------------------------------------------------------------------------
+
+def step_bytes(w, n_ctx, match_n, ring_count):
+    """Algorithmic HBM bytes of one decode step.
+
+    n_ctx: [batch] keys after the append; match_n: [batch, Hq] (-1 = miss);
+    ring_count: [batch, Hq] entries the ring held before the step.
+    Returns (total bytes, KV bytes, keys read) where keys read sums, over
+    KV groups, n - min over the group's heads of the fresh-range start."""
+    bpe, d, G, B = w.bytes_per_elem, w.head_dim, w.group, w.band
+    keys = 0
+    for b in range(w.batch):
+        n = int(n_ctx[b])
+        for g in range(w.n_kv_heads):
+            mn = match_n[b, g * G:(g + 1) * G]
+            s = np.where(mn >= 0, np.maximum(0, mn - B), 0)
+            keys += n - int(s.min())
+    kv = keys * 2 * d * bpe
+    hq = w.batch * w.n_q_heads
+    hits = int((match_n >= 0).sum())
+    ring_q = int(np.minimum(ring_count, w.window).sum()) * (d * bpe + 8)
+    reused = hits * (d * 4 + 8)
+    entry = hq * (d * bpe + d * 4 + 16)
+    qo = hq * (d * bpe + d * 4)                       # q in, out
+    append = w.batch * w.n_kv_heads * 2 * d * bpe * 2  # read k/v_new, write cache
+    return kv + ring_q + reused + entry + qo + append, kv, keys
+
+
+# ---------------------------------------------------------------------------
+# one timed point
+# ---------------------------------------------------------------------------
+
+class Layer:
+    def __init__(self, w, inp, n_steps, max_context):
+        import torch
+        from kv_cache_reuse_amd import binding as B
+        self.w, self.inp = w, inp
+        cfg = B.config_from_workload(w, max_context=max_context)
+        self.sess = B.MacSession(cfg)
+        dev = torch.device("cuda")
+        self.K = inp.k.to(dev)
+        self.V = inp.v.to(dev)
+        self.ctx = [int(c) for c in inp.contexts]
+        self.q = inp.q.to(dev)
+        self.n_steps = n_steps
+        self.t = 0
+        bidx = torch.arange(w.batch, device=dev)
+        T = inp.q.shape[0]
+        pos = torch.tensor(self.ctx, device=dev)[:, None] + torch.arange(T, device=dev)[None]
+        # per-step appended k/v, gathered once: [T, batch, Hkv, d]
+        self.k_new = self.K[bidx[:, None], :, pos].permute(1, 0, 2, 3).contiguous()
+        self.v_new = self.V[bidx[:, None], :, pos].permute(1, 0, 2, 3).contiguous()
+        hq = w.n_q_heads
+        self.match_n = torch.empty((T, w.batch, hq), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, w.batch, hq, w.head_dim), dtype=torch.float32, device=dev)
+
+    def prefill(self, upto=None):
+        for b in range(self.w.batch):
+            n = self.ctx[b] if upto is None else upto
+            self.sess.prefill(b, self.K[b, :, :n], self.V[b, :, :n])
+
+    def step(self, stream=None):
+        from kv_cache_reuse_amd import binding as B
+        t = self.t
+        s = self.sess
+        st = s._s() if stream is None else stream
+        # append + match + split-K attention + merge: one library call
+        B.mac_decode_step_append(s.ctx, self.q[t].data_ptr(), self.k_new[t].data_ptr(),
+                                 self.v_new[t].data_ptr(), s.k_cache.data_ptr(),
+                                 s.v_cache.data_ptr(), 0, self.out[t].data_ptr(),
+                                 self.match_n[t].data_ptr(), 0, st)
+        self.t += 1
+
+
+def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefill_upto=None):
+    from synth.streams import make_inputs, make_q_stream
+    Ls = []
+    for l in range(layers):
+        key = (w.name, l, per_layer)
+        if inputs_cache is not None and key in inputs_cache:
+            base = inputs_cache[key]
+            q, q64 = make_q_stream(w, p_jump=p_jump, layer=l, steps=per_layer)
+            inp = base.__class__(**{**base.__dict__, "q": q, "q64": q64})
+        else:
+            inp = make_inputs(w, p_jump=p_jump, layer=l, steps=per_layer)
+            if inputs_cache is not None:
+                inputs_cache[key] = inp
+        if prefill_upto is not None:
+            inp = inp.__class__(**{**inp.__dict__,
+                                   "contexts": np.full(w.batch, prefill_upto)})
+        mc = int(inp.contexts.max()) + per_layer if context is None else context
+        Ls.append(Layer(w, inp, per_layer, max_context=mc))
+    for L in Ls:
+        L.prefill()
+    return Ls
+
+
+def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
+              context=None, prefill_upto=None, inputs_cache=None):
+    """warmup + steps decode steps, round-robin over `layers` layer copies.
+
+    The warmup runs eagerly.  With `graph` the timed steps are captured into
+    one HIP graph (through torch.cuda.CUDAGraph, on the capture stream) and
+    the graph is replayed exactly once inside the timed region; otherwise
+    they are launched eagerly.  `kernel_timing` (eager only) brackets every
+    split-K attention launch with HIP events on the step's stream."""
+    import torch
+    from kv_cache_reuse_amd import binding as B
+    per_layer = (steps + warmup + layers - 1) // layers + 1
+    Ls = make_layers(w, p_jump, per_layer, layers, inputs_cache, context, prefill_upto)
+    torch.cuda.synchronize()
+    order = [i % layers for i in range(warmup + steps)]
+    for i in order[:warmup]:
+        Ls[i].step()
+    torch.cuda.synchronize()
+    starts = [L.t for L in Ls]
+    use_graph = graph and not kernel_timing
+    g = None
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in order[warmup:]:
+                Ls[i].step(stream=cs)
+        torch.cuda.synchronize()
+    if kernel_timing:
+        for L in Ls:
+            B.mac_profile_enable(L.sess.ctx, True)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if use_graph:
+        g.replay()
+    else:
+        for i in order[warmup:]:
+            Ls[i].step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    kms, klaunch = 0.0, 0
+    if kernel_timing:
+        for L in Ls:
+            a, n = B.mac_profile_read(L.sess.ctx)
+            kms += a
+            klaunch += n
+            B.mac_profile_enable(L.sess.ctx, False)
+    recs = []
+    for li, L in enumerate(Ls):
+        mn = L.match_n[:L.t].cpu().numpy()
+        for t in range(starts[li], L.t):
+            n_ctx = L.inp.contexts + t + 1
+            cnt = np.full((w.batch, w.n_q_heads), min(t, w.window))
+            recs.append((n_ctx, mn[t], cnt))
+    del g
+    for L in Ls:
+        L.sess.close()
+    del Ls
+    torch.cuda.empty_cache()
+    return ms, recs, kms, klaunch
+
+
+def summarize(w, ms, recs, steps):
+    tot = kv = keys = 0
+    hits = []
+    grp_all = []
+    dense = 0
+    for n_ctx, mn, cnt in recs:
+        a, b_, k = step_bytes(w, n_ctx, mn, cnt)
+        tot += a
+        kv += b_
+        keys += k
+        hits.append((mn >= 0).mean())
+        g = (mn >= 0).reshape(w.batch, w.n_kv_heads, w.group).all(axis=2)
+        grp_all.append(g.mean())
+        dense += int(n_ctx.sum()) * w.n_kv_heads * 2 * w.head_dim * w.bytes_per_elem
+    sec = ms / 1e3
+    return {
+        "hit_rate": float(np.mean(hits)),
+        "group_all_hit": float(np.mean(grp_all)),
+        "us_per_token": 1e3 * ms / steps / w.batch,
+        "us_per_step": 1e3 * ms / steps,
+        "eff_GBps": tot / sec / 1e9,
+        "kv_GBps": kv / sec / 1e9,
+        "pct_hbm_peak": 100.0 * tot / sec / 1e9 / HBM_PEAK_GBPS,
+        "dense_equiv_GBps": dense / sec / 1e9,
+        "bytes_per_step": tot / steps,
+        "kv_keys_per_step": keys / steps,
+    }
+
+
+# ---------------------------------------------------------------------------
+# cpu baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, sample_steps):
+    from threadpoolctl import threadpool_limits, threadpool_info
+    from oracle import mac_oracle as M
+    from synth.streams import make_inputs
+    cores = len(os.sched_getaffinity(0))
+    inp = make_inputs(w, p_jump=1.0, steps=sample_steps)
+    K = inp.k.float().numpy()
+    V = inp.v.float().numpy()
+    orc = M.MacOracle.for_workload(w)
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        recs = []
+        for t in range(sample_steps):
+            n = int(inp.contexts[0]) + t + 1
+            r = orc.step(0, inp.q64[t, 0], K[0], V[0], n)
+            recs.append((np.array([n]), r.match_n.reshape(1, -1).astype(np.int64),
+                         np.full((1, w.n_q_heads), min(t, w.window))))
+        sec = time.perf_counter() - t0
+    tot = sum(step_bytes(w, *r)[0] for r in recs)
+    return {
+        "value": tot / sec / 1e9, "unit": "GB/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"{sample_steps} decode steps of the {w.name} stream at jump probability 1 "
+                   f"(all misses, every KV group, {int(inp.contexts[0])}-key context), "
+                   f"fp64 NumPy oracle; {sec:.1f} s, {sec / sample_steps * 1e6:.0f} us/step"),
+        "us_per_step": sec / sample_steps * 1e6,
+    }
+
+
+def kernel_traffic():
+    """HBM traffic of the split-K kernel from the committed counter summary,
+    or None if the kernel source changed since the counters were taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    with open(PROFILE_TRAFFIC) as f:
+        tr = json.load(f)
+    with open(KERNEL_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if tr.get("kernel_sha256") != sha:
+        return None
+    return tr.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-flatness", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--points", type=str, default="")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step "
+              "is measured on one device; sharding is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth.streams import SWEEP_P_JUMP, workload
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workload("8b_128k")
+    cache = {}
+
+    # ---- headline: miss path (jump probability 1)
+    log(f"headline: {w.name} p_jump=1 steps={args.steps} warmup={args.warmup} layers={args.layers}")
+    ms, recs, _, _ = run_point(w, 1.0, args.steps, args.warmup, args.layers,
+                               inputs_cache=cache)
+    head = summarize(w, ms, recs, args.steps)
+    log(f"headline (graph): {head['us_per_token']:.1f} us/token, {head['eff_GBps']:.0f} GB/s")
+    ms_e, recs_e, _, _ = run_point(w, 1.0, args.steps, args.warmup, args.layers, graph=False,
+                                   inputs_cache=cache)
+    head_eager = summarize(w, ms_e, recs_e, args.steps)
+    log(f"headline (eager): {head_eager['us_per_token']:.1f} us/token, "
+        f"{head_eager['eff_GBps']:.0f} GB/s")
+
+    # ---- split-K kernel timing (HIP events around each launch, same stream)
+    log("kernel timing pass")
+    ms_k, recs_k, kms, klaunch = run_point(w, 1.0, args.steps, args.warmup, args.layers,
+                                           kernel_timing=True, inputs_cache=cache)
+    keys = sum(step_bytes(w, *r)[2] for r in recs_k)
+    kern_bytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(klaunch, 1)
+    kern_sec = kms / 1e3 / max(klaunch, 1)
+    achieved = kern_bytes / kern_sec / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": kernel_traffic(),
+                "kernel": "attn_partial_kernel<bf16,128,contiguous>",
+                "avg_launch_us": kern_sec * 1e6, "bytes_per_launch": kern_bytes,
+                "launches": klaunch}
+    log(f"kernel: {kern_sec * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
+
+    # ---- hit-rate sweep
+    sweep = []
+    pts = [float(x) for x in args.points.split(",")] if args.points else list(SWEEP_P_JUMP)
+    if not args.no_sweep:
+        for p in pts:
+            if p == 1.0:
+                s = dict(head)
+            else:
+                log(f"sweep point p_jump={p}")
+                msp, rp, _, _ = run_point(w, p, args.steps, args.warmup, args.layers,
+                                          inputs_cache=cache)
+                s = summarize(w, msp, rp, args.steps)
+                mse, re_, _, _ = run_point(w, p, args.steps, args.warmup, args.layers,
+                                           graph=False, inputs_cache=cache)
+                s["us_per_token_eager"] = summarize(w, mse, re_, args.steps)["us_per_token"]
+            if p == 1.0:
+                s["us_per_token_eager"] = head_eager["us_per_token"]
+            s["p_jump"] = p
+            sweep.append(s)
+            log(f"  p={p}: hit {s['hit_rate']:.3f} (group {s['group_all_hit']:.3f}) "
+                f"{s['us_per_token']:.1f} us/token (eager {s['us_per_token_eager']:.1f})")
+
+    # ---- hit-step latency over context length (no jumps: every step hits)
+    flat_steps = []
+    if not args.no_flatness:
+        flat_steps = hit_step_latency(w, cache)
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle, {args.cpu_steps} steps")
+        cpu = cpu_baseline(w, args.cpu_steps)
+        log(f"cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": head["eff_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_step"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "8b_128k: decode attention, batch 1, 32 query / 8 KV heads, "
+                               "d 128, bf16 K/V, 131072-key context, W 32, B 256, "
+                               "tau 0.5*sqrt(128), miss path (jump probability 1)",
+                   "batch": 1, "context": 131072, "layers_rotated": args.layers},
+        "launch": "timed steps captured in one HIP graph, replayed once",
+        "us_per_token": head["us_per_token"],
+        "us_per_token_eager": head_eager["us_per_token"],
+        "eager_GBps": head_eager["eff_GBps"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "sweep": sweep,
+        "flatness": flat_steps,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def hit_step_latency(w, cache, steps=128):
+    """Latency of steps in which every head hits, per context length.
+
+    Uses a query stream with no jumps (jump probability 0): after the first
+    step every head matches its previous query, so each timed step reads the
+    band and tail only.  The configured capacity is the same at every context
+    (131072 + 512 keys), so the launch grid is identical; only the prefill
+    length changes.  Steps are graph-replayed; the mean per step is reported
+    with the fraction of (head, step) decisions that hit."""
+    out = []
+    for n0 in (8192, 16384, 32768, 65536, 131072):
+        ms, recs, _, _ = run_point(w, 0.0, steps, 8, 1, inputs_cache=cache,
+                                   prefill_upto=n0, context=131072 + 512)
+        st = summarize(w, ms, recs, steps)
+        out.append({"context": n0, "us_per_step": st["us_per_step"],
+                    "hit_rate": st["hit_rate"], "group_all_hit": st["group_all_hit"],
+                    "kv_keys_per_step": st["kv_keys_per_step"]})
+        log(f"  context {n0}: {st['us_per_step']:.2f} us/step, hit {st['hit_rate']:.3f}")
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -177,6 +177,20 @@ mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre,
                            void* stream);
 
 /*
+ * mac_append_kv followed by mac_decode_step as one call (one launch fewer):
+ * k_new, v_new are device [batch][Hkv][d] (rotated keys, config dtype); the
+ * token is stored at position seq_lens_dev[b], then the query at that
+ * position attends to keys [0, seq_lens_dev[b] + 1), and seq_lens_dev[b]
+ * is incremented.  Results are bitwise identical to the two calls.  Returns
+ * MAC_ERR_CAPACITY if any sequence is full (host mirror).
+ */
+mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* page_table, float* out,
+                                  int32_t* match_ctx_out, float* dist_out,
+                                  void* stream);
+
+/*
  * Push entries into the rings directly (e.g. states computed at prefill so
  * that the first decode steps can match).  Device arrays indexed [b][h]:
  * q_pre [batch][Hq][d] dtype, o fp32 [batch][Hq][d] (normalized), m, l fp32

@@ -32,7 +32,7 @@ MAC_DTYPE_BF16 = 1
 EXPORTED = (
     "mac_kv_cache_bytes", "mac_ring_bytes", "mac_workspace_bytes", "mac_init",
     "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
-    "mac_query_cache_push", "mac_profile_enable", "mac_profile_read",
+    "mac_decode_step_append", "mac_query_cache_push", "mac_profile_enable", "mac_profile_read",
     "mac_destroy", "mac_last_error",
 )
 
@@ -69,6 +69,7 @@ def _load():
         "mac_prefill_kv": (c_int, [P, P, P, P, c_int32, P, P, c_int32, P]),
         "mac_read_kv": (c_int, [P, P, P, P, c_int32, c_int32, c_int32, P, P, P]),
         "mac_decode_step": (c_int, [P, P, P, P, P, P, P, P, P]),
+        "mac_decode_step_append": (c_int, [P, P, P, P, P, P, P, P, P, P, P]),
         "mac_query_cache_push": (c_int, [P, P, P, P, P, P, P, P, P]),
         "mac_profile_enable": (c_int, [P, c_int]),
         "mac_profile_read": (c_int, [P, POINTER(c_double), POINTER(c_int64)]),
@@ -139,6 +140,13 @@ def mac_decode_step(ctx, q_pre, k_cache, v_cache, page_table, out, match_ctx_out
                     dist_out, stream):
     _check(_lib.mac_decode_step(ctx, q_pre, k_cache, v_cache, page_table or None, out,
                                 match_ctx_out or None, dist_out or None, stream))
+
+
+def mac_decode_step_append(ctx, q_pre, k_new, v_new, k_cache, v_cache, page_table, out,
+                           match_ctx_out, dist_out, stream):
+    _check(_lib.mac_decode_step_append(ctx, q_pre, k_new, v_new, k_cache, v_cache,
+                                       page_table or None, out, match_ctx_out or None,
+                                       dist_out or None, stream))
 
 
 def mac_query_cache_push(ctx, q_pre, o, m, l, prefix_end, ctx_len, mask, stream):
@@ -250,6 +258,17 @@ class MacSession:
                         self.v_cache.data_ptr(), self._pt(), out.data_ptr(),
                         mc.data_ptr() if mc is not None else 0,
                         ds.data_ptr() if ds is not None else 0, self._s())
+        return out, mc, ds
+
+    def decode_append(self, q_pre, k_new, v_new, out=None, match_ctx=True, dist=True):
+        """Append k_new/v_new [batch, Hkv, d] and decode q_pre in one call."""
+        out = self.out if out is None else out
+        mc = self.match_ctx if match_ctx else None
+        ds = self.dist if dist else None
+        mac_decode_step_append(self.ctx, q_pre.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                               self.k_cache.data_ptr(), self.v_cache.data_ptr(), self._pt(),
+                               out.data_ptr(), mc.data_ptr() if mc is not None else 0,
+                               ds.data_ptr() if ds is not None else 0, self._s())
         return out, mc, ds
 
     def read_kv(self, seq: int, start: int, count: int):

@@ -58,19 +58,43 @@ __device__ __forceinline__ void group_starts(const StepArgs& a, int b, int kvh, 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
   const int bh = blockIdx.x;
-  const int b = bh / a.hq;
+  const int b = bh / a.hq, h = bh % a.hq;
   const int lane = threadIdx.x;
-  const int n = a.seq_lens[b];
+  int n = a.seq_lens[b];
+  if (a.k_new) {
+    // fused append: the first query head of each KV group stores the group's
+    // new key and value at position n (skipped if the sequence is full, which
+    // the host rules out except when a captured step is replayed too often)
+    const int n0 = n;
+    if (n0 >= 0 && n0 < a.geom.capacity) {
+      n = n0 + 1;
+      if (h % a.group == 0) {
+        const int kvh = h / a.group;
+        const int64_t base = tile_base_w(a.geom, a.page_table, b, kvh, n0 / kTile);
+        if (base >= 0) {
+          const size_t src = ((size_t)b * a.hkv + kvh) * D;
+          T* kc = const_cast<T*>(static_cast<const T*>(a.k_cache));
+          T* vc = const_cast<T*>(static_cast<const T*>(a.v_cache));
+          for (int e = lane; e < D; e += 64) {
+            kc[base + k_tile_offset<T>(n0 % kTile, e)] = static_cast<const T*>(a.k_new)[src + e];
+            vc[base + v_tile_offset<T>(n0 % kTile, e)] = static_cast<const T*>(a.v_new)[src + e];
+          }
+        }
+      }
+    }
+  }
+  if (h == 0 && lane == 0) a.n_step[b] = n;
   const int pos = n - 1;
   const int p_new = n - a.band > 0 ? n - a.band : 0;
   const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
 
   // Rotary embedding, rotate-half pairs (i, i + D/2), one pair per lane.
-  // Angles and the rotation in float64; the result is scaled by
-  // log2(e)/sqrt(D) so the attention kernel can use exp2.
+  // Angles and the rotation in float64 (frequencies from a float64 table);
+  // the result is scaled by log2(e)/sqrt(D) so the attention kernel can use
+  // exp2.
   if (lane < D / 2) {
     const int i = lane;
-    const double inv = pow(a.theta, -2.0 * i / D);
+    const double inv = a.inv_freq[i];
     double sn, cs;
     sincos(static_cast<double>(pos) * inv, &sn, &cs);
     const double x1 = Elem<T>::to_f(q[i]);
@@ -104,30 +128,43 @@ __global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = Elem<T>::to_f(q[c * EPL + e]);
 
+  // Entries are processed in batches of 4 x kBatch, all of a batch's loads
+  // issued before any is used, so a window of up to 32 entries costs one
+  // memory round trip.
+  constexpr int kBatch = 8;
   float best = __builtin_inff();
   int bestk = -1;
-  for (int k0 = 0; k0 < nvalid; k0 += 4) {
-    const int k = k0 + gi;
-    const bool ok = k < nvalid;
-    const int slot = ok ? ring_slot(cnt, k, R.slots) : 0;
-    float d2 = 0.f;
-    if (ok) {
+  for (int k0 = 0; k0 < nvalid; k0 += 4 * kBatch) {
+    T rv[kBatch][EPL];
+    int pe[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = k0 + 4 * u + gi;
+      const bool ok = k < nvalid;
+      const int slot = ok ? ring_slot(cnt, k, R.slots) : 0;
       const T* rq = static_cast<const T*>(R.q) + ((size_t)bh * R.slots + slot) * D + c * EPL;
 #pragma unroll
+      for (int e = 0; e < EPL; ++e) rv[u][e] = ok ? rq[e] : T(0);
+      pe[u] = ok ? R.pn[((size_t)bh * R.slots + slot) * 2] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = k0 + 4 * u + gi;
+      float d2 = 0.f;
+#pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float df = qv[e] - Elem<T>::load(rq + e);
+        const float df = qv[e] - Elem<T>::to_f(rv[u][e]);
         d2 = fmaf(df, df, d2);
       }
-    }
-    d2 += shfl_xor_f(d2, 1);
-    d2 += shfl_xor_f(d2, 2);
-    d2 += shfl_xor_f(d2, 4);
-    d2 += shfl_xor_f(d2, 8);
-    const int pe = ok ? R.pn[((size_t)bh * R.slots + slot) * 2] : -1;
-    const bool cand = ok && pe >= 0 && pe <= p_new && d2 == d2;
-    if (cand && d2 < best) {        // entries arrive newest first: ties keep the newer
-      best = d2;
-      bestk = k;
+      d2 += shfl_xor_f(d2, 1);
+      d2 += shfl_xor_f(d2, 2);
+      d2 += shfl_xor_f(d2, 4);
+      d2 += shfl_xor_f(d2, 8);
+      const bool cand = k < nvalid && pe[u] >= 0 && pe[u] <= p_new && d2 == d2;
+      if (cand && d2 < best) {      // newer entries come first: ties keep the newer
+        best = d2;
+        bestk = k;
+      }
     }
   }
   // combine the four lane groups: smallest distance, then newest entry
@@ -146,7 +183,10 @@ __global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
     hp.hit = hit ? 1 : 0;
     hp.slot = hit ? ring_slot(cnt, bestk, R.slots) : -1;
     hp.s = hit ? R.pn[((size_t)bh * R.slots + hp.slot) * 2] : 0;
-    hp.pad = 0;
+    // claim this step's slot now: the match kernel is the only reader of the
+    // counter within a step, and the merge kernel fills the slot later
+    hp.wslot = cnt % R.slots;
+    R.count[bh] = cnt + 1;
     a.plan[bh] = hp;
     if (a.match_ctx_out) a.match_ctx_out[bh] = hit ? R.pn[((size_t)bh * R.slots + hp.slot) * 2 + 1] : -1;
     if (a.dist_out) a.dist_out[bh] = bestk >= 0 ? sqrtf(best) : __builtin_inff();
@@ -178,7 +218,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(StepArgs a) {
   const int slice = blockIdx.x / n_groups;
   const int b = grp / a.hkv, kvh = grp % a.hkv;
   const int G = a.group;
-  const int n = a.seq_lens[b];
+  const int n = a.n_step[b];
   int lo, smax;
   group_starts(a, b, kvh, &lo, &smax);
   const Plan p = make_plan(lo, n, a.band, a.part.S);
@@ -407,125 +447,152 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(StepArgs a) {
 }
 
 // ===================================================================== 3 ==
-// Merge: one workgroup of 256 threads per (b, h).  Thread (sub, dim) folds
-// every nsub-th slice into its own accumulator; the subs are then combined
-// in a fixed order, so results are bitwise reproducible.
-template <int D>
-__device__ __forceinline__ void fold_slices(const StepArgs& a, size_t pbase, int G, int hl,
-                                            int i0, int i1, float M, int sub, int dim,
-                                            float* o, float* L) {
-  constexpr int NSUB = 256 / D;
-  for (int i = i0 + sub; i < i1; i += NSUB) {
-    const size_t idx = (pbase + (size_t)i * G + hl);
-    const float mi = a.part.ml[idx * 2];
-    const float li = a.part.ml[idx * 2 + 1];
-    const float w = mi == neg_inf() ? 0.f : exp2f(mi - M);
-    *o += w * a.part.o[idx * D + dim];
-    *L += w * li;
-  }
-}
+// Merge: workgroup (b, h, chunk) of 256 threads owns dims
+// [32 chunk, 32 chunk + 32) of head (b, h).  Every workgroup loads the m and
+// l of all the group's slices at once (one memory round trip), turns them
+// into weights in LDS, then its 8 x 32 threads fold the slices' o vectors
+// with independent loads.  All reductions run in a fixed order, so results
+// are bitwise reproducible.
+constexpr int kMergeDims = 32;
 
-template <int D>
-__device__ __forceinline__ float block_max(float v, float* red) {
+__device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, shfl_xor_f(v, off));
-  const int wave = threadIdx.x / 64;
-  __syncthreads();
-  if (threadIdx.x % 64 == 0) red[wave] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_f(v, off);
+  return v;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
-  constexpr int NSUB = 256 / D;
-  const int bh = blockIdx.x;
+  constexpr int NCH = D / kMergeDims;
+  constexpr int NSUB = 256 / kMergeDims;
+  const int bh = blockIdx.x / NCH, chunk = blockIdx.x % NCH;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group;
   const int kvh = h / G, hl = h % G;
-  const int n = a.seq_lens[b];
+  const int n = a.n_step[b];
   int lo, smax;
   group_starts(a, b, kvh, &lo, &smax);
   const Plan p = make_plan(lo, n, a.band, a.part.S);
   const HeadPlan hp = a.plan[bh];
   const RingView& R = a.ring;
-  const int cnt = R.count[bh];
-  const size_t pbase = ((size_t)(b * a.hkv + kvh) * a.part.S) * G;
-  const int tid = threadIdx.x, dim = tid % D, sub = tid / D;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  // fused append: publish the new length once every reader of the old one
+  // (the match kernel) has finished; no kernel of this step reads it again
+  if (a.k_new && h == 0 && chunk == 0 && tid == 0) a.seq_lens[b] = n;
+  const int npart = p.n_pre + p.n_post;
+  // partial i of this head: index (pbase + i * G)
+  const size_t pbase = (size_t)(b * a.hkv + kvh) * a.part.S * G + hl;
 
-  __shared__ float red[4];
-  __shared__ float sm_o[NSUB][D];
-  __shared__ float sm_l[NSUB];
+  __shared__ float sw[kMaxSlices];
+  __shared__ float sl[kMaxSlices];
+  __shared__ float red[4][4];
+  __shared__ float sm_pre[NSUB][kMergeDims];
+  __shared__ float sm_post[NSUB][kMergeDims];
 
-  // reused state (natural base in the ring -> log2 units of the scaled score)
-  float mr = neg_inf(), lr = 0.f, orr = 0.f;
+  // reused state: ring stores natural-log m and normalized o
+  float mr = neg_inf(), lr = 0.f;
+  size_t re = 0;
   if (hp.hit) {
-    const size_t e = (size_t)bh * R.slots + hp.slot;
-    mr = R.ml[e * 2] * static_cast<float>(kLog2e);
-    lr = R.ml[e * 2 + 1];
-    orr = R.o[e * D + dim] * lr;
-    if (R.ml[e * 2] == neg_inf()) mr = neg_inf();
+    re = (size_t)bh * R.slots + hp.slot;
+    const float mn = R.ml[re * 2];
+    lr = R.ml[re * 2 + 1];
+    mr = mn == neg_inf() ? neg_inf() : mn * static_cast<float>(kLog2e);
   }
 
-  // ---- prefix = merge(reused, slices [0, n_pre))
-  float mloc = mr;
-  for (int i = tid; i < p.n_pre; i += 256) mloc = fmaxf(mloc, a.part.ml[(pbase + (size_t)i * G + hl) * 2]);
-  const float M = block_max<D>(mloc, red);
-  float o = 0.f, L = 0.f;
-  if (sub == 0 && hp.hit) {
-    const float w = mr == neg_inf() ? 0.f : exp2f(mr - M);
-    o = w * orr;
-    L = w * lr;
+  // ---- m, l of every slice; maxima of the prefix and the tail slices
+  float mp = neg_inf(), mq = neg_inf();
+  for (int i = tid; i < npart; i += 256) {
+    const size_t idx = pbase + (size_t)i * G;
+    const float mi = a.part.ml[idx * 2];
+    sw[i] = mi;
+    sl[i] = a.part.ml[idx * 2 + 1];
+    if (i < p.n_pre) mp = fmaxf(mp, mi);
+    else mq = fmaxf(mq, mi);
   }
-  fold_slices<D>(a, pbase, G, hl, 0, p.n_pre, M, sub, dim, &o, &L);
-  sm_o[sub][dim] = o;
-  if (dim == 0) sm_l[sub] = L;
+  mp = wave_max(mp);
+  mq = wave_max(mq);
+  if (lane == 0) {
+    red[0][wave] = mp;
+    red[1][wave] = mq;
+  }
   __syncthreads();
-  float po = 0.f, pL = 0.f;
+  const float Mpre = fmaxf(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])), mr);
+  const float Mpost = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  const float Mall = fmaxf(Mpre, Mpost);
+
+  // ---- weights (prefix slices relative to Mpre, tail slices to Mall), l sums
+  float lp = 0.f, lq = 0.f;
+  for (int i = tid; i < npart; i += 256) {
+    const float mi = sw[i];
+    const bool pre = i < p.n_pre;
+    const float w = mi == neg_inf() ? 0.f : exp2f(mi - (pre ? Mpre : Mall));
+    sw[i] = w;
+    if (pre) lp += w * sl[i];
+    else lq += w * sl[i];
+  }
+  lp = wave_sum(lp);
+  lq = wave_sum(lq);
+  __syncthreads();
+  if (lane == 0) {
+    red[2][wave] = lp;
+    red[3][wave] = lq;
+  }
+  __syncthreads();
+  const float wr = (hp.hit && mr != neg_inf()) ? exp2f(mr - Mpre) : 0.f;
+  const float Lpre = ((red[2][0] + red[2][1]) + (red[2][2] + red[2][3])) + wr * lr;
+  const float Lpost = (red[3][0] + red[3][1]) + (red[3][2] + red[3][3]);
+
+  // ---- o: thread (sub, dd) folds slices sub, sub + 8, ...
+  const int sub = tid / kMergeDims, dd = tid % kMergeDims;
+  const int dim = chunk * kMergeDims + dd;
+  float op = 0.f, oq = 0.f;
+  for (int i0 = sub; i0 < npart; i0 += 4 * NSUB) {
+    float ov[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NSUB;
+      ov[u] = i < npart ? a.part.o[(pbase + (size_t)i * G) * D + dim] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NSUB;
+      if (i < npart) {
+        if (i < p.n_pre) op += sw[i] * ov[u];
+        else oq += sw[i] * ov[u];
+      }
+    }
+  }
+  if (sub == 0 && hp.hit) op += wr * lr * R.o[re * D + dim];
+  sm_pre[sub][dd] = op;
+  sm_post[sub][dd] = oq;
+  __syncthreads();
+  if (sub != 0) return;
+  float po = 0.f, qo = 0.f;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    po += sm_o[s][dim];
-    pL += sm_l[s];
+    po += sm_pre[s][dd];
+    qo += sm_post[s][dd];
   }
 
   // ---- the head's new ring entry: (q_pre, prefix state, p_new, n)
-  const int wslot = cnt % R.slots;
-  const size_t we = (size_t)bh * R.slots + wslot;
-  if (sub == 0) {
-    R.o[we * D + dim] = pL == 0.f ? 0.f : po / pL;
-    static_cast<T*>(R.q)[we * D + dim] = static_cast<const T*>(a.q_pre)[(size_t)bh * D + dim];
-    if (dim == 0) {
-      R.ml[we * 2] = pL == 0.f ? neg_inf() : M * kLn2;
-      R.ml[we * 2 + 1] = pL;
-      R.pn[we * 2] = p.mid;
-      R.pn[we * 2 + 1] = n;
-      R.count[bh] = cnt + 1;
-    }
+  const size_t we = (size_t)bh * R.slots + hp.wslot;
+  R.o[we * D + dim] = Lpre == 0.f ? 0.f : po / Lpre;
+  static_cast<T*>(R.q)[we * D + dim] = static_cast<const T*>(a.q_pre)[(size_t)bh * D + dim];
+  if (chunk == 0 && dd == 0) {
+    R.ml[we * 2] = Lpre == 0.f ? neg_inf() : Mpre * kLn2;
+    R.ml[we * 2 + 1] = Lpre;
+    R.pn[we * 2] = p.mid;
+    R.pn[we * 2 + 1] = n;
   }
 
-  // ---- out = merge(prefix, slices [n_pre, n_pre + n_post))
-  const int i0 = p.n_pre, i1 = p.n_pre + p.n_post;
-  float m2 = pL == 0.f ? neg_inf() : M;
-  for (int i = i0; i < i1; ++i) m2 = fmaxf(m2, a.part.ml[(pbase + (size_t)i * G + hl) * 2]);
-  float oo = 0.f, LL = 0.f;
-  if (sub == 0) {
-    const float w = (pL == 0.f) ? 0.f : exp2f(M - m2);
-    oo = w * po;
-    LL = w * pL;
-  }
-  fold_slices<D>(a, pbase, G, hl, i0, i1, m2, sub, dim, &oo, &LL);
-  __syncthreads();
-  sm_o[sub][dim] = oo;
-  if (dim == 0) sm_l[sub] = LL;
-  __syncthreads();
-  if (sub == 0) {
-    float fo = 0.f, fL = 0.f;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      fo += sm_o[s][dim];
-      fL += sm_l[s];
-    }
-    a.out[(size_t)bh * D + dim] = fL == 0.f ? 0.f : fo / fL;
-  }
+  // ---- out = merge(prefix, tail slices)
+  const float sc = Mpre == neg_inf() ? 0.f : exp2f(Mpre - Mall);
+  const float num = po * sc + qo;
+  const float den = Lpre * sc + Lpost;
+  a.out[(size_t)bh * D + dim] = den == 0.f ? 0.f : num / den;
 }
 
 // ============================================================ KV layout ==
@@ -534,10 +601,14 @@ __global__ __launch_bounds__(256) void append_kernel(T* kc, T* vc, const int32_t
                                                      const T* vn, int32_t* seq_lens, KvGeom geom) {
   const int b = blockIdx.x;
   const int n0 = seq_lens[b];
+  // a full sequence (possible only if a captured step is replayed past the
+  // capacity the host checked) is left unchanged
+  if (n0 < 0 || n0 >= geom.capacity) return;
   const int t = n0 / kTile, r = n0 % kTile;
   for (int idx = threadIdx.x; idx < geom.hkv * D; idx += blockDim.x) {
     const int g = idx / D, dim = idx % D;
-    const int64_t base = tile_base(geom, pt, b, g, t);
+    const int64_t base = tile_base_w(geom, pt, b, g, t);
+    if (base < 0) continue;
     const size_t src = ((size_t)b * geom.hkv + g) * D + dim;
     kc[base + k_tile_offset<T>(r, dim)] = kn[src];
     vc[base + v_tile_offset<T>(r, dim)] = vn[src];
@@ -555,7 +626,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(T* kc, T* vc, const int32_
   if (idx >= (int64_t)count * D) return;
   const int tok = static_cast<int>(idx / D), dim = static_cast<int>(idx % D);
   const int pos = seq_lens[seq] + tok;
-  const int64_t base = tile_base(geom, pt, seq, g, pos / kTile);
+  if (pos < 0 || pos >= geom.capacity) return;
+  const int64_t base = tile_base_w(geom, pt, seq, g, pos / kTile);
+  if (base < 0) return;
   const size_t src = ((size_t)g * count + tok) * D + dim;
   kc[base + k_tile_offset<T>(pos % kTile, dim)] = ks[src];
   vc[base + v_tile_offset<T>(pos % kTile, dim)] = vs[src];
@@ -575,7 +648,21 @@ __global__ __launch_bounds__(256) void read_kernel(const T* kc, const T* vc, con
   vd[dst] = vc[base + v_tile_offset<T>(pos % kTile, dim)];
 }
 
-__global__ void add_len_kernel(int32_t* seq_lens, int seq, int count) { seq_lens[seq] += count; }
+__global__ void add_len_kernel(int32_t* seq_lens, int seq, int count, int capacity) {
+  const int n = seq_lens[seq] + count;
+  seq_lens[seq] = n < capacity ? n : capacity;
+}
+
+// Rotary frequencies theta^(-2i/d), i < d/2, in float64 (once, at init).
+__global__ void inv_freq_kernel(double* out, int d, double theta) {
+  const int i = threadIdx.x;
+  if (i < d / 2) out[i] = pow(theta, -2.0 * i / d);
+}
+
+hipError_t launch_inv_freq(double* out, int d, double theta, hipStream_t st) {
+  hipLaunchKernelGGL(inv_freq_kernel, dim3(1), dim3(64), 0, st, out, d, theta);
+  return hipGetLastError();
+}
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -626,7 +713,7 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   MAC_DISPATCH(dtype, d, L_ATTN);
 #undef L_ATTN
   if (ev1) (void)hipEventRecord(ev1, st);
-#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq), dim3(256), 0, st, a)
+#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq * (D / kMergeDims)), dim3(256), 0, st, a)
   MAC_DISPATCH(dtype, d, L_MERGE);
 #undef L_MERGE
   return hipGetLastError();
@@ -653,7 +740,7 @@ hipError_t launch_prefill(void* kc, void* vc, const int32_t* pt, const void* ks,
                      (const T*)vs, seq_lens, seq, count, geom)
   MAC_DISPATCH(dtype, geom.d, L_PRE);
 #undef L_PRE
-  hipLaunchKernelGGL(add_len_kernel, dim3(1), dim3(1), 0, st, seq_lens, seq, count);
+  hipLaunchKernelGGL(add_len_kernel, dim3(1), dim3(1), 0, st, seq_lens, seq, count, geom.capacity);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ mac_status ok() {
   return MAC_OK;
 }
 
+// Split-K workgroups a miss step aims for: two 256-thread workgroups per
+// compute unit of a 256-CU part (the attention kernel's occupancy).
+constexpr int kTargetWorkgroups = 512;
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -42,7 +46,7 @@ struct Layout {
   // ring
   size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
   // workspace
-  size_t w_plan, w_qfrag, w_po, w_pml, ws_bytes;
+  size_t w_plan, w_qfrag, w_po, w_pml, w_nstep, w_invf, ws_bytes;
   int slices;
   int64_t capacity;     // keys per sequence
   int tiles_per_seq;    // contiguous cache
@@ -71,8 +75,9 @@ mac_status check_config(const mac_config* c) {
   if (!(c->tau >= 0.f)) return fail(MAC_ERR_INVALID_ARG, "tau must be >= 0 (got %g)", (double)c->tau);
   if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
     return fail(MAC_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
-  if (c->max_slices != 0 && c->max_slices < 2)
-    return fail(MAC_ERR_INVALID_ARG, "max_slices must be 0 (default) or >= 2 (got %d)", c->max_slices);
+  if (c->max_slices != 0 && (c->max_slices < 2 || c->max_slices > mac::kMaxSlices))
+    return fail(MAC_ERR_INVALID_ARG, "max_slices must be 0 (default) or in [2, %d] (got %d)",
+                mac::kMaxSlices, c->max_slices);
   if (c->page_size == 0) {
     if (c->max_context < 1)
       return fail(MAC_ERR_INVALID_ARG, "max_context must be >= 1 (got %d)", c->max_context);
@@ -106,11 +111,11 @@ Layout layout(const mac_config* c) {
   const int groups = c->batch * c->n_kv_heads;
   int S = c->max_slices;
   if (S == 0) {
-    // about four 256-thread workgroups per compute unit on a 256-CU part,
     // never more slices than the longest context can fill
-    S = mac::ceil_div(1024, groups);
+    S = mac::ceil_div(kTargetWorkgroups, groups);
     const int cap = (int)((L.capacity + mac::kSliceMin - 1) / mac::kSliceMin) + 1;
     if (S > cap) S = cap;
+    if (S > mac::kMaxSlices) S = mac::kMaxSlices;
     if (S < 2) S = 2;
   }
   L.slices = S;
@@ -120,6 +125,8 @@ Layout layout(const mac_config* c) {
   L.w_qfrag = off; off = align256(off + bh * d * 4);
   L.w_po = off;    off = align256(off + (size_t)groups * S * G * d * 4);
   L.w_pml = off;   off = align256(off + (size_t)groups * S * G * 2 * 4);
+  L.w_nstep = off; off = align256(off + (size_t)c->batch * 4);
+  L.w_invf = off;  off = align256(off + (d / 2) * 8);
   L.ws_bytes = off;
   return L;
 }
@@ -156,6 +163,8 @@ struct mac_ctx {
     g.tiles_per_seq = L.tiles_per_seq;
     g.paged = cfg.page_size ? 1 : 0;
     g.max_pages = cfg.max_pages_per_seq;
+    g.n_pages = cfg.n_pages;
+    g.capacity = (int)L.capacity;
     return g;
   }
 };
@@ -239,6 +248,9 @@ mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t*
   hipError_t e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
                                       cfg->batch * cfg->n_q_heads, 0,
                                       static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = mac::launch_inv_freq(reinterpret_cast<double*>(ctx->ws + L.w_invf), cfg->head_dim,
+                             cfg->rope_theta, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     delete ctx;
     return device_fail(nullptr, e, "mac_init: clearing the ring");
@@ -308,9 +320,14 @@ mac_status mac_read_kv(mac_ctx* ctx, const void* k_cache, const void* v_cache,
   return ok();
 }
 
-mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
-                           const void* v_cache, const int32_t* page_table, float* out,
-                           int32_t* match_ctx_out, float* dist_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of mac_decode_step and mac_decode_step_append (k_new != null).
+mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, float* out, int32_t* match_ctx_out,
+                       float* dist_out, const void* k_new, const void* v_new, void* stream) {
   mac_status s;
   if ((s = check_ctx(ctx))) return s;
   if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
@@ -318,9 +335,18 @@ mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
   if ((s = check_ptr(out, "out"))) return s;
   if ((s = check_ptr(match_ctx_out, "match_ctx_out", false))) return s;
   if ((s = check_ptr(dist_out, "dist_out", false))) return s;
-  for (int b = 0; b < ctx->cfg.batch; ++b)
-    if (ctx->mirror[b] < 1)
-      return fail(MAC_ERR_INVALID_ARG, "sequence %d has no keys: append before decoding", b);
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  if (fused) {
+    if ((s = check_ptr(k_new, "k_new"))) return s;
+    if ((s = check_ptr(v_new, "v_new"))) return s;
+    for (int b = 0; b < ctx->cfg.batch; ++b)
+      if (ctx->mirror[b] + 1 > ctx->L.capacity)
+        return fail(MAC_ERR_CAPACITY, "sequence %d is full (%lld keys)", b, (long long)ctx->mirror[b]);
+  } else {
+    for (int b = 0; b < ctx->cfg.batch; ++b)
+      if (ctx->mirror[b] < 1)
+        return fail(MAC_ERR_INVALID_ARG, "sequence %d has no keys: append before decoding", b);
+  }
 
   const mac_config& c = ctx->cfg;
   const Layout& L = ctx->L;
@@ -330,6 +356,10 @@ mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
   a.v_cache = v_cache;
   a.page_table = page_table;
   a.seq_lens = ctx->seq_lens_dev;
+  a.n_step = reinterpret_cast<int32_t*>(ctx->ws + L.w_nstep);
+  a.inv_freq = reinterpret_cast<const double*>(ctx->ws + L.w_invf);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.out = out;
   a.match_ctx_out = match_ctx_out;
   a.dist_out = dist_out;
@@ -364,7 +394,31 @@ mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
   hipError_t e = mac::launch_step(a, c.dtype, c.head_dim, c.page_size ? 1 : 0,
                                   static_cast<hipStream_t>(stream), e0, e1);
   if (e != hipSuccess) return device_fail(ctx, e, "mac_decode_step");
+  if (fused)
+    for (auto& n : ctx->mirror) ++n;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, float* out,
+                           int32_t* match_ctx_out, float* dist_out, void* stream) {
+  return decode_impl(ctx, q_pre, k_cache, v_cache, page_table, out, match_ctx_out, dist_out,
+                     nullptr, nullptr, stream);
+}
+
+mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* page_table, float* out, int32_t* match_ctx_out,
+                                  float* dist_out, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if (!k_new || !v_new) return fail(MAC_ERR_INVALID_ARG, "k_new and v_new are required");
+  return decode_impl(ctx, q_pre, k_cache, v_cache, page_table, out, match_ctx_out, dist_out,
+                     k_new, v_new, stream);
 }
 
 mac_status mac_query_cache_push(mac_ctx* ctx, const void* q_pre, const float* o, const float* m,

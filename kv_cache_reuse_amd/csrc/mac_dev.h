@@ -11,7 +11,8 @@
 namespace mac {
 
 constexpr int kTile = 16;        // tokens per KV tile (= page size when paged)
-constexpr int kSliceMin = 256;   // fewest keys a split-K slice is given
+constexpr int kSliceMin = 64;    // fewest keys a split-K slice is given (4 tiles)
+constexpr int kMaxSlices = 1024; // most split-K slices per KV group
 constexpr int kMaxGroup = 16;    // query heads per KV head: the MFMA N width
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -76,15 +77,40 @@ struct KvGeom {
   int tiles_per_seq;     // contiguous: ceil(max_context / 16)
   int paged;             // 1: tile t of sequence b is page_table[b*mp + t]
   int max_pages;         // paged: page-table columns
+  int n_pages;           // paged: pages in the pool
+  int capacity;          // keys per sequence
 };
 
-// Element offset of the start of tile t of (b, g).
+// Page of tile t of sequence b; -1 if the table entry is outside the pool.
+__device__ __forceinline__ int64_t page_of(const KvGeom& g, const int32_t* pt, int b, int t) {
+  const int32_t page = pt[int64_t(b) * g.max_pages + t];
+  return (page >= 0 && page < g.n_pages) ? page : -1;
+}
+
+// Element offset of the start of tile t of (b, g) for reading.  A page-table
+// entry outside the pool is clamped into it, so a corrupt table gives wrong
+// values but never an out-of-bounds access.
 __device__ __forceinline__ int64_t tile_base(const KvGeom& g, const int32_t* pt,
                                              int b, int kvh, int t) {
   const int64_t tile_elems = int64_t(kTile) * g.d;
   if (g.paged) {
-    const int64_t page = pt[int64_t(b) * g.max_pages + t];
+    int64_t page = page_of(g, pt, b, t);
+    if (page < 0) page = 0;
     return (page * g.hkv + kvh) * tile_elems;
+  }
+  return ((int64_t(b) * g.hkv + kvh) * g.tiles_per_seq + t) * tile_elems;
+}
+
+// Element offset of tile t of (b, g) for writing, or -1 when position
+// t * 16 is not writable (past the capacity or an invalid page): writes there
+// are dropped instead of landing outside the cache.
+__device__ __forceinline__ int64_t tile_base_w(const KvGeom& g, const int32_t* pt,
+                                               int b, int kvh, int t) {
+  if (t < 0 || int64_t(t) * kTile >= g.capacity) return -1;
+  const int64_t tile_elems = int64_t(kTile) * g.d;
+  if (g.paged) {
+    const int64_t page = page_of(g, pt, b, t);
+    return page < 0 ? -1 : (page * g.hkv + kvh) * tile_elems;
   }
   return ((int64_t(b) * g.hkv + kvh) * g.tiles_per_seq + t) * tile_elems;
 }
@@ -108,7 +134,7 @@ struct HeadPlan {   // written by the match kernel, one per (b, h)
   int32_t hit;      // 1 on a hit
   int32_t slot;     // ring slot of the matched entry (valid on a hit)
   int32_t s;        // start of the fresh key range
-  int32_t pad;
+  int32_t wslot;    // ring slot this step's entry goes to
 };
 
 // Split-K plan of one KV group: fresh keys [lo, hi) split at mid = p_new
@@ -165,7 +191,11 @@ struct StepArgs {
   const void* k_cache;
   const void* v_cache;
   const int32_t* page_table;
-  const int32_t* seq_lens;  // [batch]
+  int32_t* seq_lens;        // [batch] device lengths
+  int32_t* n_step;          // [batch] keys this step attends to (set by match)
+  const double* inv_freq;   // [D/2] theta^(-2i/D), float64
+  const void* k_new;        // fused append: [batch][Hkv][D] dtype, else null
+  const void* v_new;
   float* out;               // [batch][Hq][D]
   int32_t* match_ctx_out;   // nullable
   float* dist_out;          // nullable

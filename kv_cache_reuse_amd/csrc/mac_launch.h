@@ -26,6 +26,8 @@ hipError_t launch_read(const void* kc, const void* vc, const int32_t* pt, void* 
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 
+hipError_t launch_inv_freq(double* out, int d, double theta, hipStream_t st);
+
 hipError_t launch_push(const RingView& R, int batch, int hq, int d, int dtype, const void* q,
                        const float* o, const float* m, const float* l, const int32_t* pe,
                        const int32_t* ne, const uint8_t* mask, hipStream_t st);

@@ -57,7 +57,8 @@ def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] 
 
 
 def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 0,
-            paged: Optional[bool] = None, q_override=None, poison: bool = False) -> GpuRun:
+            paged: Optional[bool] = None, q_override=None, poison: bool = False,
+            fused: bool = False) -> GpuRun:
     """Prefill every sequence, then `steps` x (append, decode).  `record`
     selects the steps whose outputs are copied back (default: all)."""
     T = inp.q.shape[0] if steps is None else steps
@@ -79,8 +80,11 @@ def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 
         pos = ctx_t + t
         k_new = K[bidx, :, pos].contiguous()          # [batch, Hkv, d]
         v_new = V[bidx, :, pos].contiguous()
-        sess.append(k_new, v_new)
-        out, mc, ds = sess.decode(q_all[t].contiguous())
+        if fused:
+            out, mc, ds = sess.decode_append(q_all[t].contiguous(), k_new, v_new)
+        else:
+            sess.append(k_new, v_new)
+            out, mc, ds = sess.decode(q_all[t].contiguous())
         if record is None or t in record:
             res.out[t] = out.float().cpu().numpy().copy()
             res.match_n[t] = mc.cpu().numpy().copy()

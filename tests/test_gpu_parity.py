@@ -77,6 +77,37 @@ def test_stale_cache_slots_do_not_leak(name):
     assert_report(rep, f"poison:{name}", 0)
 
 
+@pytest.mark.parametrize("name", ["tiny_full", "8b_128k_p05", "paged_b8_small", "70b_small",
+                                  "ctx1"])
+def test_fused_append_decode_every_step(name):
+    base, kw = SMALL[name]
+    w = workload(base, **kw)
+    inp = make_inputs(w)
+    say(f"[fused:{name}]")
+    gpu = run_gpu(w, inp, fused=True, poison=True)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"fused:{name}", 0 if w.window == 0 else 1)
+
+
+def test_fused_equals_separate_calls_bitwise():
+    w = workload("paged_b8", ctx_range=(600, 1400), steps=20)
+    inp = make_inputs(w)
+    a = run_gpu(w, inp, fused=True)
+    b = run_gpu(w, inp, fused=False)
+    for t in a.out:
+        np.testing.assert_array_equal(a.out[t], b.out[t])
+        np.testing.assert_array_equal(a.match_n[t], b.match_n[t])
+        np.testing.assert_array_equal(a.dist[t], b.dist[t])
+    for bb in range(w.batch):
+        n = int(inp.contexts[bb]) + w.steps
+        ka, va = a.session.read_kv(bb, 0, n)
+        kb, vb = b.session.read_kv(bb, 0, n)
+        torch.cuda.synchronize()
+        assert torch.equal(ka, kb) and torch.equal(va, vb)
+        assert torch.equal(ka.cpu(), inp.k[bb, :, :n])
+    assert torch.equal(a.session.seq_lens.cpu(), b.session.seq_lens.cpu())
+
+
 def test_paged_equals_contiguous_bitwise():
     w = workload("paged_b8", ctx_range=(500, 1500), steps=16)
     inp = make_inputs(w)
