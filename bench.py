@@ -39,6 +39,7 @@ METRIC = ("decode-attention µs/token + effective KV GB/s (% HBM peak) at 128K, 
           "hit-rate sweep")
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_attn_partial_8b_128k.json")
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", "kernels.hip")
+COPY_CAL_BYTES = 512 * 1024 * 1024
 
 
 def log(msg):
@@ -296,6 +297,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--points", type=str, default="")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 512 MiB device-to-device (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step "
@@ -309,6 +312,15 @@ def main():
         sys.exit(1)
     w = workload("8b_128k")
     cache = {}
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling hardware byte counters
+        src = torch.empty(COPY_CAL_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {COPY_CAL_BYTES} bytes read and written")
+        del src, dst
 
     # ---- headline: miss path (jump probability 1)
     log(f"headline: {w.name} p_jump=1 steps={args.steps} warmup={args.warmup} layers={args.layers}")

@@ -8,7 +8,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/kernels.hip", "csrc/mac_api.hip"]
+SOURCES = ["csrc/step.hip", "csrc/kv_ring.hip", "csrc/mac_api.hip"]
 OUT = os.path.join(HERE, "libmac.so")
 
 FLAGS = [

@@ -35,9 +35,9 @@ mac_status ok() {
   return MAC_OK;
 }
 
-// Split-K workgroups a miss step aims for: two 256-thread workgroups per
-// compute unit of a 256-CU part (the attention kernel's occupancy).
-constexpr int kTargetWorkgroups = 512;
+// Split-K workgroups a miss step aims for: one 256-thread workgroup per
+// compute unit of a 256-CU part.
+constexpr int kTargetWorkgroups = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -46,7 +46,7 @@ struct Layout {
   // ring
   size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
   // workspace
-  size_t w_plan, w_qfrag, w_po, w_pml, w_nstep, w_invf, ws_bytes;
+  size_t w_po, w_pml, w_heads, w_invf, ws_bytes;
   int slices;
   int64_t capacity;     // keys per sequence
   int tiles_per_seq;    // contiguous cache
@@ -118,14 +118,13 @@ Layout layout(const mac_config* c) {
     if (S > mac::kMaxSlices) S = mac::kMaxSlices;
     if (S < 2) S = 2;
   }
-  L.slices = S;
   const size_t G = c->n_q_heads / c->n_kv_heads;
+  if (S * G > (size_t)mac::kMergeCap) S = mac::kMergeCap / (int)G;
+  L.slices = S;
   off = 0;
-  L.w_plan = off;  off = align256(off + bh * sizeof(mac::HeadPlan));
-  L.w_qfrag = off; off = align256(off + bh * d * 4);
-  L.w_po = off;    off = align256(off + (size_t)groups * S * G * d * 4);
-  L.w_pml = off;   off = align256(off + (size_t)groups * S * G * 2 * 4);
-  L.w_nstep = off; off = align256(off + (size_t)c->batch * 4);
+  L.w_po = off;      off = align256(off + (size_t)groups * S * G * d * 4);
+  L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
+  L.w_heads = off;   off = align256(off + bh * sizeof(mac::HeadState));
   L.w_invf = off;  off = align256(off + (d / 2) * 8);
   L.ws_bytes = off;
   return L;
@@ -356,15 +355,13 @@ mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, con
   a.v_cache = v_cache;
   a.page_table = page_table;
   a.seq_lens = ctx->seq_lens_dev;
-  a.n_step = reinterpret_cast<int32_t*>(ctx->ws + L.w_nstep);
   a.inv_freq = reinterpret_cast<const double*>(ctx->ws + L.w_invf);
   a.k_new = k_new;
   a.v_new = v_new;
   a.out = out;
   a.match_ctx_out = match_ctx_out;
   a.dist_out = dist_out;
-  a.plan = reinterpret_cast<mac::HeadPlan*>(ctx->ws + L.w_plan);
-  a.qfrag = ctx->ws + L.w_qfrag;
+  a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
   a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
   a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
   a.part.S = L.slices;

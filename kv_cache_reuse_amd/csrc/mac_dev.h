@@ -14,9 +14,19 @@ constexpr int kTile = 16;        // tokens per KV tile (= page size when paged)
 constexpr int kSliceMin = 64;    // fewest keys a split-K slice is given (4 tiles)
 constexpr int kMaxSlices = 1024; // most split-K slices per KV group
 constexpr int kMaxGroup = 16;    // query heads per KV head: the MFMA N width
+constexpr int kMergeCap = 2048;  // most (query head, slice) pairs one merge holds
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Instantiate FN(T, D) for the (dtype, head_dim) pairs the library builds.
+#define MAC_DISPATCH(dtype, d, FN)                                         \
+  do {                                                                     \
+    if ((dtype) == 1 && (d) == 128) { FN(uint16_t, 128); }                 \
+    else if ((dtype) == 1 && (d) == 64) { FN(uint16_t, 64); }              \
+    else if ((dtype) == 0 && (d) == 128) { FN(float, 128); }               \
+    else { FN(float, 64); }                                                \
+  } while (0)
 
 // ---------------------------------------------------------------- bf16 ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
@@ -130,11 +140,17 @@ struct RingView {
 };
 
 // ---------------------------------------------------------- workspace ----
-struct HeadPlan {   // written by the match kernel, one per (b, h)
-  int32_t hit;      // 1 on a hit
-  int32_t slot;     // ring slot of the matched entry (valid on a hit)
-  int32_t s;        // start of the fresh key range
-  int32_t wslot;    // ring slot this step's entry goes to
+// Match result of one query head for one step, recorded by the step kernel
+// for the merge kernel.
+struct HeadState {
+  int hit;       // 1 on a hit
+  int slot;      // ring slot of the matched entry
+  int s;         // start of the fresh key range
+  int cnt;       // ring pushes before this step
+  int match_n;   // context length of the matched entry, -1 on a miss
+  float dist;    // distance of the best candidate, +inf if none
+  int n;         // keys of the sequence after this step's append
+  int pad;
 };
 
 // Split-K plan of one KV group: fresh keys [lo, hi) split at mid = p_new
@@ -192,15 +208,13 @@ struct StepArgs {
   const void* v_cache;
   const int32_t* page_table;
   int32_t* seq_lens;        // [batch] device lengths
-  int32_t* n_step;          // [batch] keys this step attends to (set by match)
   const double* inv_freq;   // [D/2] theta^(-2i/D), float64
   const void* k_new;        // fused append: [batch][Hkv][D] dtype, else null
   const void* v_new;
   float* out;               // [batch][Hq][D]
   int32_t* match_ctx_out;   // nullable
   float* dist_out;          // nullable
-  HeadPlan* plan;           // [batch*Hq]
-  void* qfrag;              // [batch*Hq][D] hi bf16 then [batch*Hq][D] lo bf16; or fp32
+  HeadState* heads;         // [batch*Hq] match results of the step
   PartialView part;
   RingView ring;
   KvGeom geom;

@@ -1,0 +1,745 @@
+// libmac decode step for gfx950 (MI355X): two launches per MAC-Attention step.
+//
+// Method: "MAC-Attention: a Match-Amend-Complete Scheme for Fast and
+// Accurate Attention Computation", abstract: a match stage (pre-RoPE L2
+// matching over a short window of recent queries), an amend stage (the reused
+// attention is rectified by recomputing a band of keys at the match
+// boundary), a complete stage (fresh attention over the KV tail fused with the
+// rest through a numerically stable merge); on a hit the cost does not depend
+// on the context length.
+//
+// Two launches per step, so that the only cross-workgroup hand-off goes
+// through a kernel boundary (no device-wide fences or atomics):
+//
+//  step_kernel, one 256-thread workgroup per (slice, KV group), slice-major,
+//  over a fixed number of slices S per group (the launch is the same for every
+//  step and can be captured in a graph):
+//   A. read the sequence length; for each of the group's G query heads rotate
+//      the query (float64 angles) and match the pre-RoPE query against the
+//      ring (one wave per head, 16 lanes per ring slot); derive the group's
+//      split-K plan and this workgroup's slice of keys.  The slice-0
+//      workgroup records every head's match result for the merge.
+//   B. with a non-empty slice: split-K attention on the matrix cores, one
+//      partial state (o, m, l) per head.  With a fused append, the workgroup
+//      whose slice holds the new token stores it in the cache and patches it
+//      into its own registers.
+//  merge_kernel, one workgroup per query head: log-sum-exp merge of the
+//  reused state and the slices, the head's new ring entry and its output;
+//  with a fused append it also publishes the new length.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mac_dev.h"
+#include "mac_launch.h"
+
+#ifndef MAC_ATTN_PREFETCH
+#define MAC_ATTN_PREFETCH 1
+#endif
+
+namespace mac {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kMatchSlotsPerGroup = 16;   // ring slots per 16-lane group per round
+constexpr int kPrefetch = MAC_ATTN_PREFETCH;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+// Sum over each 16-lane row of the wave, result in every lane of the row:
+// DPP row rotations (VALU, no LDS round trip) by 8, 4, 2, 1.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, shfl_xor_f(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_f(v, off);
+  return v;
+}
+
+template <int D>
+struct Shared {
+  HeadState head[kMaxGroup];
+  // rotated, scaled queries: bf16 hi/lo halves or fp32
+  __attribute__((aligned(16))) unsigned char q[2 * kMaxGroup * D * 2];
+  // phase B epilogue: the four waves' states
+  float m[4][kMaxGroup];
+  float l[4][kMaxGroup];
+  float o[4][kMaxGroup][D + 1];
+};
+
+// =========================================================== phase A ====
+// One wave: rotary embedding and ring match of query head h (index hi in the
+// group).  All loads are issued before any value is used.
+template <typename T, int D>
+__device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int b, int h, int hi,
+                                           int lane, int n, int p_new) {
+  constexpr int EPL = D / 16;
+  const int bh = b * a.hq + h;
+  const int gi = lane / 16, c = lane % 16;
+  const RingView& R = a.ring;
+  const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
+  const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
+  const int32_t* rpn = R.pn + (size_t)bh * R.slots * 2;
+
+  // a lane's D/16 elements of one query row as 2, 4 or 8 dwords, one vector
+  // load (rows start 16-byte aligned, so the lane's piece is aligned too)
+  constexpr int NW = EPL * (int)sizeof(T) / 4;
+  auto load_row = [&](const T* src, uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+      const u2 v = *reinterpret_cast<const u2*>(src);
+      w[0] = v.x; w[1] = v.y;
+    } else if constexpr (NW == 4) {
+      const u4 v = *reinterpret_cast<const u4*>(src);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      const u4 v0 = reinterpret_cast<const u4*>(src)[0];
+      const u4 v1 = reinterpret_cast<const u4*>(src)[1];
+      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    }
+  };
+  auto elem = [&](const uint32_t (&w)[NW], int e) -> float {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
+    else return __uint_as_float(w[e]);
+  };
+
+  const int cnt = R.count[bh];
+  const bool rot = lane < D / 2;
+  const double inv = rot ? a.inv_freq[lane] : 0.0;
+  const T q1 = rot ? q[lane] : T(0);
+  const T q2 = rot ? q[lane + D / 2] : T(0);
+  uint32_t qw[NW];
+  load_row(q + c * EPL, qw);
+  // every slot index is clamped into the ring; slots past W + 1 are dropped
+  // by the candidate test (their age is set to W + 1)
+  uint32_t rw[kMatchSlotsPerGroup][NW];
+  int pe[kMatchSlotsPerGroup];
+#pragma unroll
+  for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
+    const int s = gi + 4 * u;
+    const int sc = s < R.slots ? s : 0;
+    load_row(rq + (size_t)sc * D + c * EPL, rw[u]);
+    pe[u] = rpn[sc * 2];
+  }
+
+  // rotate-half pairs (i, i + D/2): float64 angle and rotation, result scaled
+  // by log2(e)/sqrt(D) so that the attention can use exp2
+  if (rot) {
+    const int i = lane;
+    double sn, cs;
+    sincos(static_cast<double>(n - 1) * inv, &sn, &cs);
+    const double x1 = Elem<T>::to_f(q1), x2 = Elem<T>::to_f(q2);
+    const double sc = kLog2e / sqrt(static_cast<double>(D));
+    const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
+    const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
+    if constexpr (sizeof(T) == 2) {
+      uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * D;
+      uint16_t* ql = reinterpret_cast<uint16_t*>(sh.q) + (kMaxGroup + hi) * D;
+      const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
+      qh[i] = h1;
+      qh[i + D / 2] = h2;
+      ql[i] = f32_to_bf16(r1 - bf16_to_f32(h1));
+      ql[i + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
+    } else {
+      float* qs = reinterpret_cast<float*>(sh.q) + hi * D;
+      qs[i] = r1;
+      qs[i + D / 2] = r2;
+    }
+  }
+
+  // Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
+  // candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
+  // smallest squared distance, then smallest k (the newest entry).
+  const int nvalid = cnt < R.window ? cnt : R.window;
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = elem(qw, e);
+  float best = __builtin_inff();
+  int bestk = -1;
+  for (int s0 = 0; s0 < R.slots; s0 += 4 * kMatchSlotsPerGroup) {
+    if (s0 > 0) {        // windows of 64 or more: further rounds of loads
+#pragma unroll
+      for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
+        const int s = s0 + gi + 4 * u;
+        const int sc = s < R.slots ? s : 0;
+        load_row(rq + (size_t)sc * D + c * EPL, rw[u]);
+        pe[u] = rpn[sc * 2];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
+      const int s = s0 + gi + 4 * u;
+      float d2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float df = qv[e] - elem(rw[u], e);
+        d2 = fmaf(df, df, d2);
+      }
+      d2 = row16_sum(d2);
+      const int k = s < R.slots ? (cnt - 1 - s + R.slots) % R.slots : R.slots;
+      const bool cand = k < nvalid && pe[u] >= 0 && pe[u] <= p_new && d2 == d2;
+      if (cand && (d2 < best || (d2 == best && k < bestk))) {
+        best = d2;
+        bestk = k;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float ob = shfl_xor_f(best, off);
+    const int ok = shfl_xor_i(bestk, off);
+    if (ok >= 0 && (bestk < 0 || ob < best || (ob == best && ok < bestk))) {
+      best = ob;
+      bestk = ok;
+    }
+  }
+  if (lane == 0) {
+    const bool hit = bestk >= 0 && best < a.tau2;
+    HeadState hs;
+    hs.hit = hit ? 1 : 0;
+    hs.slot = hit ? (cnt - 1 - bestk) % R.slots : -1;
+    hs.s = hit ? rpn[hs.slot * 2] : 0;
+    hs.cnt = cnt;
+    hs.match_n = hit ? rpn[hs.slot * 2 + 1] : -1;
+    hs.dist = bestk >= 0 ? sqrtf(best) : __builtin_inff();
+    hs.n = n;
+    hs.pad = 0;
+    sh.head[hi] = hs;
+  }
+}
+
+// ========================================================== the kernel ==
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int E = 16 / (int)sizeof(T);
+  constexpr int NL = D * (int)sizeof(T) / 64;   // 1 KiB blocks per tile, K and V each
+  constexpr int NQ = BF ? 2 * NL : 4 * NL;      // QK MFMA steps per tile
+  constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
+
+  __shared__ Shared<D> sh;
+  const int n_groups = a.batch * a.hkv;
+  const int grp = blockIdx.x % n_groups;
+  const int slice = blockIdx.x / n_groups;
+  const int b = grp / a.hkv, kvh = grp % a.hkv;
+  const int G = a.group;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const bool fused = a.k_new != nullptr;
+
+  // ---------------------------------------------------------------- A ----
+  const int n0 = a.seq_lens[b];
+  const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
+  const int n = append ? n0 + 1 : n0;
+  const int p_new = n - a.band > 0 ? n - a.band : 0;
+  for (int hi = wave; hi < G; hi += 4) match_head<T, D>(a, sh, b, kvh * G + hi, hi, lane, n, p_new);
+  __syncthreads();
+  int lo = sh.head[0].s, smax = sh.head[0].s;
+  for (int i = 1; i < G; ++i) {
+    lo = min(lo, sh.head[i].s);
+    smax = max(smax, sh.head[i].s);
+  }
+  const Plan p = make_plan(lo, n, a.band, a.part.S);
+  const int nact = p.n_pre + p.n_post;
+  if (slice == 0 && tid < G) {
+    const int bh = b * a.hq + kvh * G + tid;
+    a.heads[bh] = sh.head[tid];
+    if (a.match_ctx_out) a.match_ctx_out[bh] = sh.head[tid].match_n;
+    if (a.dist_out) a.dist_out[bh] = sh.head[tid].dist;
+  }
+
+  // ---------------------------------------------------------------- B ----
+  if (slice < nact) {
+    int ka, ke;
+    slice_range(p, slice, &ka, &ke);
+    const int lg = lane / 16, col = lane % 16;
+    const bool hv = col < G;
+    const int s_col = hv ? sh.head[col].s : 0;
+
+    // query fragments (B operand of S = K Q^T) from LDS; zero for padding heads
+    v4s qh[BF ? NQ : 1], ql[BF ? NQ : 1];
+    float qf[BF ? 1 : NQ];
+    if constexpr (BF) {
+      const uint16_t* qhs = reinterpret_cast<const uint16_t*>(sh.q) + col * D;
+      const uint16_t* qls = reinterpret_cast<const uint16_t*>(sh.q) + (kMaxGroup + col) * D;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int d0 = 8 * (4 * j + lg) + 4 * hh;
+          v4s x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+          if (hv) {
+            x = *reinterpret_cast<const v4s*>(qhs + d0);
+            y = *reinterpret_cast<const v4s*>(qls + d0);
+          }
+          qh[2 * j + hh] = x;
+          ql[2 * j + hh] = y;
+        }
+    } else {
+      const float* qss = reinterpret_cast<const float*>(sh.q) + col * D;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * j + e] = hv ? qss[4 * (4 * j + lg) + e] : 0.f;
+    }
+
+    const T* kc = static_cast<const T*>(a.k_cache);
+    const T* vc = static_cast<const T*>(a.v_cache);
+    KvGeom geom = a.geom;
+    geom.paged = PAGED ? 1 : 0;
+
+    // fused append: the slice holding the new token (always the last one)
+    // stores it and patches it into its own fragments
+    const bool patcher = append && slice == nact - 1;
+    const int tnew = (n - 1) / kTile, rnew = (n - 1) % kTile;
+    u4 kpatch[NL];
+    T vpatch[NL][E / 4];
+    if (patcher) {
+      const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
+      const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) kpatch[j] = *reinterpret_cast<const u4*>(kn + E * (4 * j + lg));
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int th = 0; th < E / 4; ++th) vpatch[i][th] = vn[16 * ((E / 4) * i + th) + col];
+      if (wave == 0) {
+        const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
+        if (base >= 0) {
+          T* kw = const_cast<T*>(kc);
+          T* vw = const_cast<T*>(vc);
+          for (int e = lane; e < D; e += 64) {
+            kw[base + k_tile_offset<T>(rnew, e)] = kn[e];
+            vw[base + v_tile_offset<T>(rnew, e)] = vn[e];
+          }
+        }
+      }
+    }
+
+    v4f acc[NCT];
+#pragma unroll
+    for (int i = 0; i < NCT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    float m = neg_inf();
+    float lsum = 0.f;
+    const int t0 = ka / kTile, t1 = (ke + kTile - 1) / kTile;
+
+    auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
+      const int64_t base = tile_base(geom, a.page_table, b, kvh, tt);
+      const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
+      const u4* vp = reinterpret_cast<const u4*>(vc + base) + lane;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        kk[j] = kp[64 * j];
+        vv[j] = vp[64 * j];
+      }
+    };
+
+    auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
+      if (patcher && tt == tnew) {
+        // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
+        if (col == rnew) {
+#pragma unroll
+          for (int j = 0; j < NL; ++j) kr[j] = kpatch[j];
+        }
+        if (lg == rnew / 4) {
+#pragma unroll
+          for (int i = 0; i < NL; ++i)
+#pragma unroll
+            for (int th = 0; th < E / 4; ++th) {
+              const int e = th * 4 + rnew % 4;           // element in the 16 bytes
+              uint32_t val, mask;
+              int dw;
+              if constexpr (BF) {
+                const int shift = (e & 1) * 16;
+                dw = e >> 1;
+                val = static_cast<uint32_t>(vpatch[i][th]) << shift;
+                mask = 0xffffu << shift;
+              } else {
+                dw = e;
+                val = __float_as_uint(vpatch[i][th]);
+                mask = 0xffffffffu;
+              }
+              vr[i].x = dw == 0 ? (vr[i].x & ~mask) | val : vr[i].x;
+              vr[i].y = dw == 1 ? (vr[i].y & ~mask) | val : vr[i].y;
+              vr[i].z = dw == 2 ? (vr[i].z & ~mask) | val : vr[i].z;
+              vr[i].w = dw == 3 ? (vr[i].w & ~mask) | val : vr[i].w;
+            }
+        }
+      }
+      // ---- S = K Q^T: lane holds tokens 4 lg + r of head col
+      v4f s = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const u2 k01 = kr[j].xy, k23 = kr[j].zw;
+          const v4s ka0 = __builtin_bit_cast(v4s, k01);
+          const v4s ka1 = __builtin_bit_cast(v4s, k23);
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka0, qh[2 * j], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka0, ql[2 * j], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka1, qh[2 * j + 1], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka1, ql[2 * j + 1], s, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[j][e]), qf[4 * j + e], s, 0, 0, 0);
+      }
+
+      // ---- mask tokens outside [ka, ke) and, per head, before its start
+      const int tok0 = tt * kTile;
+      const bool full = tok0 >= ka && tok0 + kTile <= ke && tok0 >= smax;
+      if (!full) {
+        // tokens outside [ka, ke) may be unwritten slots past the end of the
+        // sequence: zero their values too, so that 0 * (stale NaN/Inf) cannot
+        // enter the PV product (lane's V fragment = its score tokens)
+        uint32_t keep[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = tok0 + 4 * lg + r;
+          const bool in = kk >= ka && kk < ke;
+          keep[r] = in ? 0xffffffffu : 0u;
+          if (!in || kk < s_col) s[r] = neg_inf();
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          if constexpr (BF) {
+            const uint32_t m01 = (keep[0] & 0xffffu) | (keep[1] & 0xffff0000u);
+            const uint32_t m23 = (keep[2] & 0xffffu) | (keep[3] & 0xffff0000u);
+            vr[i].x &= m01;
+            vr[i].y &= m23;
+            vr[i].z &= m01;
+            vr[i].w &= m23;
+          } else {
+            vr[i].x &= keep[0];
+            vr[i].y &= keep[1];
+            vr[i].z &= keep[2];
+            vr[i].w &= keep[3];
+          }
+        }
+      }
+
+      // ---- online softmax, base 2
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      if (mnew > m) {
+        const float alpha = exp2f(m - mnew);
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) acc[i] *= alpha;
+        lsum *= alpha;
+        m = mnew;
+      }
+      const float mref = m == neg_inf() ? 0.f : m;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = exp2f(s[r] - mref);
+        lsum += pr[r];
+      }
+
+      // ---- O^T += V^T P^T
+      if constexpr (BF) {
+        v4s ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t hb = f32_to_bf16(pr[r]);
+          ph[r] = static_cast<short>(hb);
+          pl[r] = static_cast<short>(f32_to_bf16(pr[r] - bf16_to_f32(hb)));
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          // materialize the halves first: a bit cast taken straight from a
+          // swizzled lvalue (vr[i].zw) reads the vector's first 8 bytes
+          const u2 v01 = vr[i].xy, v23 = vr[i].zw;
+          const v4s va0 = __builtin_bit_cast(v4s, v01);
+          const v4s va1 = __builtin_bit_cast(v4s, v23);
+          acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va0, ph, acc[2 * i], 0, 0, 0);
+          acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va0, pl, acc[2 * i], 0, 0, 0);
+          acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va1, ph, acc[2 * i + 1], 0, 0, 0);
+          acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va1, pl, acc[2 * i + 1], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vr[i][r]), pr[r], acc[i], 0, 0, 0);
+      }
+    };
+
+    // Wave w takes tiles t0 + w, t0 + w + 4, ...; the next tiles are loaded
+    // while the current one is processed.  Prefetch loads are unconditional
+    // (an index past the slice is clamped to its last tile, an in-bounds
+    // cache hit): a load under a branch leaves the outstanding-load count
+    // unknown at the join, and the compiler then waits for every load,
+    // prefetches included, before the current tile's math.
+    const int tlast = t1 - 1;
+    int t = t0 + wave;
+    if (t < t1) {
+      if constexpr (kPrefetch == 1) {
+        u4 kA[NL], vA[NL], kB[NL], vB[NL];
+        load_tile(t, kA, vA);
+        for (; t < t1; t += 8) {
+          load_tile(min(t + 4, tlast), kB, vB);
+          process(t, kA, vA);
+          if (t + 4 >= t1) break;
+          load_tile(min(t + 8, tlast), kA, vA);
+          process(t + 4, kB, vB);
+        }
+      } else {
+        u4 kA[NL], vA[NL], kB[NL], vB[NL], kC[NL], vC[NL];
+        load_tile(t, kA, vA);
+        load_tile(min(t + 4, tlast), kB, vB);
+        for (; t < t1; t += 12) {
+          load_tile(min(t + 8, tlast), kC, vC);
+          process(t, kA, vA);
+          if (t + 4 >= t1) break;
+          load_tile(min(t + 12, tlast), kA, vA);
+          process(t + 4, kB, vB);
+          if (t + 8 >= t1) break;
+          load_tile(min(t + 16, tlast), kB, vB);
+          process(t + 8, kC, vC);
+        }
+      }
+    }
+    lsum += shfl_xor_f(lsum, 16);
+    lsum += shfl_xor_f(lsum, 32);
+
+    // ---- the four waves' states -> the slice's partial state
+    if (lg == 0) {
+      sh.m[wave][col] = m;
+      sh.l[wave][col] = lsum;
+    }
+#pragma unroll
+    for (int i = 0; i < NCT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.o[wave][col][16 * i + 4 * lg + r] = acc[i][r];
+    __syncthreads();
+    const size_t pbase = ((size_t)grp * a.part.S + slice) * G;
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int hh = idx / D, dim = idx % D;
+      float Mx = sh.m[0][hh];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, sh.m[w][hh]);
+      float o = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = sh.m[w][hh];
+        const float sc = mw == neg_inf() ? 0.f : exp2f(mw - Mx);
+        o += sc * sh.o[w][hh][dim];
+        L += sc * sh.l[w][hh];
+      }
+      a.part.o[(pbase + hh) * D + dim] = o;
+      if (dim == 0) {
+        a.part.ml[(pbase + hh) * 2] = Mx;
+        a.part.ml[(pbase + hh) * 2 + 1] = L;
+      }
+    }
+  }
+
+}
+
+// ========================================================= merge kernel ==
+// One 256-thread workgroup per query head (b, h): log-sum-exp merge of the
+// reused state and the group's slices, the head's new ring entry and its
+// output.  The m and l of every slice are loaded in one round trip and turned
+// into weights in LDS; thread (sub, quad) then folds every NSUB-th slice's
+// 4 consecutive output dims with 16-byte loads.  All reductions run in a
+// fixed order, so results are bitwise reproducible.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
+  constexpr int NQ4 = D / 4;            // float4 quads of one head's output
+  constexpr int NSUB = 256 / NQ4;       // slice subsets folded in parallel
+  constexpr int kBatch = 8;             // loads in flight per thread per round
+  const int bh = blockIdx.x;
+  const int b = bh / a.hq, h = bh % a.hq;
+  const int G = a.group, kvh = h / G, hi = h % G;
+  const int S = a.part.S, grp = b * a.hkv + kvh;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const RingView& R = a.ring;
+  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  const HeadState hs = hsg[hi];
+  const int n = hs.n;
+  int lo = hsg[0].s;
+  for (int i = 1; i < G; ++i) lo = min(lo, hsg[i].s);
+  const Plan p = make_plan(lo, n, a.band, S);
+  const int npart = p.n_pre + p.n_post;
+
+  __shared__ float sw[kMaxSlices];
+  __shared__ float sl[kMaxSlices];
+  __shared__ float red[4][4];
+  __shared__ float4 rp[NSUB][NQ4];
+  __shared__ float4 rq[NSUB][NQ4];
+
+  // reused state: the ring stores natural-log m and normalized o
+  float mr = neg_inf(), lr = 0.f;
+  size_t re = 0;
+  if (hs.hit) {
+    re = (size_t)bh * R.slots + hs.slot;
+    const float mn = R.ml[re * 2];
+    lr = R.ml[re * 2 + 1];
+    mr = mn == neg_inf() ? neg_inf() : mn * static_cast<float>(kLog2e);
+  }
+
+  // ---- the first kBatch slices' outputs of this thread are loaded together
+  // with every slice's m and l (one round trip for both)
+  const int sub = tid / NQ4, d4 = tid % NQ4;
+  float4 v0[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int k = sub + u * NSUB;
+    const size_t idx = ((size_t)grp * S + k) * G + hi;
+    v0[u] = k < npart ? reinterpret_cast<const float4*>(a.part.o + idx * D)[d4]
+                      : float4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- m, l of every slice; maxima of the prefix and the tail slices
+  float mp = neg_inf(), mq = neg_inf();
+  for (int k = tid; k < npart; k += 256) {
+    const size_t idx = ((size_t)grp * S + k) * G + hi;
+    const float mk = a.part.ml[idx * 2];
+    sw[k] = mk;
+    sl[k] = a.part.ml[idx * 2 + 1];
+    if (k < p.n_pre) mp = fmaxf(mp, mk);
+    else mq = fmaxf(mq, mk);
+  }
+  mp = wave_max(mp);
+  mq = wave_max(mq);
+  if (lane == 0) {
+    red[0][wave] = mp;
+    red[1][wave] = mq;
+  }
+  __syncthreads();
+  const float Mpre = fmaxf(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])), mr);
+  const float Mall = fmaxf(Mpre, fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+
+  // ---- weights: prefix slices relative to Mpre, tail slices to Mall
+  float lp = 0.f, lq = 0.f;
+  for (int k = tid; k < npart; k += 256) {
+    const bool pre = k < p.n_pre;
+    const float mk = sw[k];
+    const float w = mk == neg_inf() ? 0.f : exp2f(mk - (pre ? Mpre : Mall));
+    sw[k] = w;
+    if (pre) lp += w * sl[k];
+    else lq += w * sl[k];
+  }
+  lp = wave_sum(lp);
+  lq = wave_sum(lq);
+  if (lane == 0) {
+    red[2][wave] = lp;
+    red[3][wave] = lq;
+  }
+  __syncthreads();
+  const float wr = (hs.hit && mr != neg_inf()) ? exp2f(mr - Mpre) : 0.f;
+  const float Lpre = ((red[2][0] + red[2][1]) + (red[2][2] + red[2][3])) + wr * lr;
+  const float Lpost = (red[3][0] + red[3][1]) + (red[3][2] + red[3][3]);
+
+  // ---- o
+  float4 op = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = sub; k0 < npart; k0 += NSUB * kBatch) {
+    float4 v[kBatch];
+    if (k0 == sub) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = v0[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + u * NSUB;
+        const size_t idx = ((size_t)grp * S + k) * G + hi;
+        v[u] = k < npart ? reinterpret_cast<const float4*>(a.part.o + idx * D)[d4]
+                         : float4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = k0 + u * NSUB;
+      if (k < npart) {
+        const float w = sw[k];
+        if (k < p.n_pre) {
+          op.x += w * v[u].x; op.y += w * v[u].y; op.z += w * v[u].z; op.w += w * v[u].w;
+        } else {
+          oq.x += w * v[u].x; oq.y += w * v[u].y; oq.z += w * v[u].z; oq.w += w * v[u].w;
+        }
+      }
+    }
+  }
+  rp[sub][d4] = op;
+  rq[sub][d4] = oq;
+  __syncthreads();
+  if (sub != 0) return;
+  float4 po = {0.f, 0.f, 0.f, 0.f}, qo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    po.x += rp[s][d4].x; po.y += rp[s][d4].y; po.z += rp[s][d4].z; po.w += rp[s][d4].w;
+    qo.x += rq[s][d4].x; qo.y += rq[s][d4].y; qo.z += rq[s][d4].z; qo.w += rq[s][d4].w;
+  }
+  if (hs.hit) {
+    const float4 ro = reinterpret_cast<const float4*>(R.o + re * D)[d4];
+    const float f = wr * lr;
+    po.x += f * ro.x; po.y += f * ro.y; po.z += f * ro.z; po.w += f * ro.w;
+  }
+
+  // ---- the head's new ring entry: (q_pre, prefix state, p_new, n)
+  const size_t we = (size_t)bh * R.slots + hs.cnt % R.slots;
+  const float4 eo = Lpre == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
+                                : float4{po.x / Lpre, po.y / Lpre, po.z / Lpre, po.w / Lpre};
+  reinterpret_cast<float4*>(R.o + we * D)[d4] = eo;
+  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + 4 * d4;
+  T* qdst = static_cast<T*>(R.q) + we * D + 4 * d4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qdst[e] = qsrc[e];
+
+  // ---- out = merge(prefix, tail slices)
+  const float sc = Mpre == neg_inf() ? 0.f : exp2f(Mpre - Mall);
+  const float den = Lpre * sc + Lpost;
+  const float4 o4 = den == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
+                               : float4{(po.x * sc + qo.x) / den, (po.y * sc + qo.y) / den,
+                                        (po.z * sc + qo.z) / den, (po.w * sc + qo.w) / den};
+  reinterpret_cast<float4*>(a.out + (size_t)bh * D)[d4] = o4;
+  if (d4 == 0) {
+    R.ml[we * 2] = Lpre == 0.f ? neg_inf() : Mpre * kLn2;
+    R.ml[we * 2 + 1] = Lpre;
+    R.pn[we * 2] = p.mid;
+    R.pn[we * 2 + 1] = n;
+    R.count[bh] = hs.cnt + 1;
+    // fused append: publish the new length (no kernel of this step reads it
+    // after the step kernel)
+    if (a.k_new && h == 0) a.seq_lens[b] = n;
+  }
+}
+
+hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
+                       hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0) (void)hipEventRecord(ev0, st);
+  const int grid = a.batch * a.hkv * a.part.S;
+#define L_STEP(T, D)                                                                           \
+  if (paged) hipLaunchKernelGGL((step_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, a);  \
+  else hipLaunchKernelGGL((step_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, a)
+  MAC_DISPATCH(dtype, d, L_STEP);
+#undef L_STEP
+  if (ev1) (void)hipEventRecord(ev1, st);
+#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq), dim3(256), 0, st, a)
+  MAC_DISPATCH(dtype, d, L_MERGE);
+#undef L_MERGE
+  return hipGetLastError();
+}
+
+}  // namespace mac
