@@ -81,6 +81,8 @@ struct Shared {
   float m[4][kMaxGroup];
   float l[4][kMaxGroup];
   float o[4][kMaxGroup][D + 1];
+  // fused append: the new token's key and value
+  __attribute__((aligned(16))) unsigned char patch[2 * D * 4];
 };
 
 // =========================================================== phase A ====
@@ -307,17 +309,18 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     // stores it and patches it into its own fragments
     const bool patcher = append && slice == nact - 1;
     const int tnew = (n - 1) / kTile, rnew = (n - 1) % kTile;
-    u4 kpatch[NL];
-    T vpatch[NL][E / 4];
+    // the new token's key and value are staged in LDS (not registers, which
+    // would stay live through the whole tile loop)
+    T* pk = reinterpret_cast<T*>(sh.patch);
+    T* pv = pk + D;
     if (patcher) {
       const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
       const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) kpatch[j] = *reinterpret_cast<const u4*>(kn + E * (4 * j + lg));
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int th = 0; th < E / 4; ++th) vpatch[i][th] = vn[16 * ((E / 4) * i + th) + col];
+      for (int e = tid; e < D; e += 256) {
+        pk[e] = kn[e];
+        pv[e] = vn[e];
+      }
+      __syncthreads();
       if (wave == 0) {
         const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
         if (base >= 0) {
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
         if (col == rnew) {
 #pragma unroll
-          for (int j = 0; j < NL; ++j) kr[j] = kpatch[j];
+          for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(pk + E * (4 * j + lg));
         }
         if (lg == rnew / 4) {
 #pragma unroll
@@ -367,11 +370,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
               if constexpr (BF) {
                 const int shift = (e & 1) * 16;
                 dw = e >> 1;
-                val = static_cast<uint32_t>(vpatch[i][th]) << shift;
+                val = static_cast<uint32_t>(pv[16 * ((E / 4) * i + th) + col]) << shift;
                 mask = 0xffffu << shift;
               } else {
                 dw = e;
-                val = __float_as_uint(vpatch[i][th]);
+                val = __float_as_uint(pv[16 * ((E / 4) * i + th) + col]);
                 mask = 0xffffffffu;
               }
               vr[i].x = dw == 0 ? (vr[i].x & ~mask) | val : vr[i].x;
