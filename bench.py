@@ -14,7 +14,7 @@ Printed: one JSON line.  `value` is the effective KV bandwidth of the miss
 path (every step misses: jump probability 1), i.e. algorithmic bytes / time;
 `sweep` holds the hit-rate sweep (jump probability 1, 0.5, 0.2, 0.05) with
 us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
-latency at contexts 8K..128K; `roofline` the split-K kernel's achieved
+latency at contexts 8K..128K; `roofline` the step kernel's achieved
 bandwidth from HIP events around its launches; `cpu_baseline` the fp64
 oracle timed on a bounded sample of the same workload on the host cores.
 """
@@ -37,8 +37,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = ("decode-attention µs/token + effective KV GB/s (% HBM peak) at 128K, "
           "hit-rate sweep")
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_attn_partial_8b_128k.json")
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", "kernels.hip")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_step_kernel_8b_128k.json")
+# sources the step kernel is compiled from: the stored counter figures are
+# only valid for the kernel they were taken on
+KERNEL_SRCS = [os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", f)
+               for f in ("step.hip", "mac_dev.h")]
+ROOFLINE_KERNEL = "mac::step_kernel<bf16,128,contiguous>"
 COPY_CAL_BYTES = 512 * 1024 * 1024
 
 
@@ -272,16 +276,22 @@ def cpu_baseline(w, sample_steps):
     }
 
 
+def kernel_sha256():
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def kernel_traffic():
-    """HBM traffic of the split-K kernel from the committed counter summary,
+    """HBM traffic of the step kernel from the committed counter summary,
     or None if the kernel source changed since the counters were taken."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     with open(PROFILE_TRAFFIC) as f:
         tr = json.load(f)
-    with open(KERNEL_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if tr.get("kernel_sha256") != sha:
+    if tr.get("kernel_sha256") != kernel_sha256():
         return None
     return tr.get("bytes_per_launch")
 
@@ -334,7 +344,7 @@ def main():
     log(f"headline (eager): {head_eager['us_per_token']:.1f} us/token, "
         f"{head_eager['eff_GBps']:.0f} GB/s")
 
-    # ---- split-K kernel timing (HIP events around each launch, same stream)
+    # ---- step kernel timing (HIP events around each launch, on its stream)
     log("kernel timing pass")
     ms_k, recs_k, kms, klaunch = run_point(w, 1.0, args.steps, args.warmup, args.layers,
                                            kernel_timing=True, inputs_cache=cache)
@@ -344,7 +354,7 @@ def main():
     achieved = kern_bytes / kern_sec / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": kernel_traffic(),
-                "kernel": "attn_partial_kernel<bf16,128,contiguous>",
+                "kernel": ROOFLINE_KERNEL,
                 "avg_launch_us": kern_sec * 1e6, "bytes_per_launch": kern_bytes,
                 "launches": klaunch}
     log(f"kernel: {kern_sec * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
