@@ -155,7 +155,10 @@ struct HeadState {
 
 // Split-K plan of one KV group: fresh keys [lo, hi) split at mid = p_new
 // into n_pre slices over [lo, mid) and n_post slices over [mid, hi).
-// Interior boundaries fall on 16-token tile edges.
+// Interior boundaries fall on 16-token tile edges.  Slice order: the n_post
+// slices come first (indices 0 .. n_post - 1): their keys do not depend on
+// the match, so a workgroup can start loading them before it knows the match
+// result; the n_pre slices follow.
 struct Plan {
   int lo, mid, hi, n_pre, n_post;
 };
@@ -183,15 +186,17 @@ __host__ __device__ __forceinline__ int split_bound(int a, int e, int n, int i) 
   return x > a ? x : a;
 }
 
+__host__ __device__ __forceinline__ bool slice_is_pre(const Plan& p, int i) { return i >= p.n_post; }
+
 // Key range [*a, *e) of slice i of a plan (i < n_pre + n_post).
 __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* a, int* e) {
-  if (i < p.n_pre) {
-    *a = split_bound(p.lo, p.mid, p.n_pre, i);
-    *e = split_bound(p.lo, p.mid, p.n_pre, i + 1);
+  if (i < p.n_post) {
+    *a = split_bound(p.mid, p.hi, p.n_post, i);
+    *e = split_bound(p.mid, p.hi, p.n_post, i + 1);
   } else {
-    const int k = i - p.n_pre;
-    *a = split_bound(p.mid, p.hi, p.n_post, k);
-    *e = split_bound(p.mid, p.hi, p.n_post, k + 1);
+    const int k = i - p.n_post;
+    *a = split_bound(p.lo, p.mid, p.n_pre, k);
+    *e = split_bound(p.lo, p.mid, p.n_pre, k + 1);
   }
 }
 

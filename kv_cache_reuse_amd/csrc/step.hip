@@ -20,9 +20,12 @@
 //      split-K plan and this workgroup's slice of keys.  The slice-0
 //      workgroup records every head's match result for the merge.
 //   B. with a non-empty slice: split-K attention on the matrix cores, one
-//      partial state (o, m, l) per head.  With a fused append, the workgroup
+//      partial state (o, m, l) per head.  Each wave's first tile under the
+//      plan a miss would give is loaded while the match runs, and kept when
+//      the real plan gives the slice the same keys (always on a miss, and for
+//      the slices after p_new on a hit).  With a fused append, the workgroup
 //      whose slice holds the new token stores it in the cache and patches it
-//      into its own registers.
+//      into the tile it loads.
 //  merge_kernel, one workgroup per query head: log-sum-exp merge of the
 //  reused state and the slices, the head's new ring entry and its output;
 //  with a fused append it also publishes the new length.
@@ -88,9 +91,9 @@ struct Shared {
 // =========================================================== phase A ====
 // One wave: rotary embedding and ring match of query head h (index hi in the
 // group).  All loads are issued before any value is used.
-template <typename T, int D>
+template <typename T, int D, typename Mid>
 __device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int b, int h, int hi,
-                                           int lane, int n, int p_new) {
+                                           int lane, int n, int p_new, Mid&& mid) {
   constexpr int EPL = D / 16;
   const int bh = b * a.hq + h;
   const int gi = lane / 16, c = lane % 16;
@@ -139,6 +142,7 @@ __device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int
     load_row(rq + (size_t)sc * D + c * EPL, rw[u]);
     pe[u] = rpn[sc * 2];
   }
+  mid();   // further loads, issued behind the ring's
 
   // rotate-half pairs (i, i + D/2): float64 angle and rotation, result scaled
   // by log2(e)/sqrt(D) so that the attention can use exp2
@@ -244,12 +248,41 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const bool fused = a.k_new != nullptr;
 
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  KvGeom geom = a.geom;
+  geom.paged = PAGED ? 1 : 0;
+  auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
+    const int64_t base = tile_base(geom, a.page_table, b, kvh, tt);
+    const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
+    const u4* vp = reinterpret_cast<const u4*>(vc + base) + lane;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      kk[j] = kp[64 * j];
+      vv[j] = vp[64 * j];
+    }
+  };
+
   // ---------------------------------------------------------------- A ----
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
   const int p_new = n - a.band > 0 ? n - a.band : 0;
-  for (int hi = wave; hi < G; hi += 4) match_head<T, D>(a, sh, b, kvh * G + hi, hi, lane, n, p_new);
+  // The group's plan when any of its heads misses does not depend on the
+  // match: this wave's first tile under it is loaded while the match runs
+  // and kept if the real plan gives the slice the same keys.
+  const Plan ps = make_plan(0, n, a.band, a.part.S);
+  int ska = 0, ske = 0;
+  if (slice < ps.n_pre + ps.n_post) slice_range(ps, slice, &ska, &ske);
+  const int st0 = ska / kTile, st1 = (ske + kTile - 1) / kTile;
+  int tspec = st0 + wave < st1 ? st0 + wave : st1 - 1;
+  if (tspec < 0) tspec = 0;
+  u4 kA[NL], vA[NL];
+  auto spec = [&] { load_tile(tspec, kA, vA); };
+  if (wave < G) match_head<T, D>(a, sh, b, kvh * G + wave, wave, lane, n, p_new, spec);
+  else spec();
+  for (int hi = wave + 4; hi < G; hi += 4)
+    match_head<T, D>(a, sh, b, kvh * G + hi, hi, lane, n, p_new, [] {});
   __syncthreads();
   int lo = sh.head[0].s, smax = sh.head[0].s;
   for (int i = 1; i < G; ++i) {
@@ -300,14 +333,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         for (int e = 0; e < 4; ++e) qf[4 * j + e] = hv ? qss[4 * (4 * j + lg) + e] : 0.f;
     }
 
-    const T* kc = static_cast<const T*>(a.k_cache);
-    const T* vc = static_cast<const T*>(a.v_cache);
-    KvGeom geom = a.geom;
-    geom.paged = PAGED ? 1 : 0;
-
-    // fused append: the slice holding the new token (always the last one)
-    // stores it and patches it into its own fragments
-    const bool patcher = append && slice == nact - 1;
+    // fused append: the slice holding the new token (the last post slice,
+    // or the last pre slice when there are none) stores it and patches it
+    // into the tile it loads
+    const bool patcher = append && slice == (p.n_post > 0 ? p.n_post - 1 : nact - 1);
     const int tnew = (n - 1) / kTile, rnew = (n - 1) % kTile;
     // the new token's key and value are staged in LDS (not registers, which
     // would stay live through the whole tile loop)
@@ -340,17 +369,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     float m = neg_inf();
     float lsum = 0.f;
     const int t0 = ka / kTile, t1 = (ke + kTile - 1) / kTile;
-
-    auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
-      const int64_t base = tile_base(geom, a.page_table, b, kvh, tt);
-      const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
-      const u4* vp = reinterpret_cast<const u4*>(vc + base) + lane;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        kk[j] = kp[64 * j];
-        vv[j] = vp[64 * j];
-      }
-    };
 
     auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
       if (patcher && tt == tnew) {
@@ -498,8 +516,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     int t = t0 + wave;
     if (t < t1) {
       if constexpr (kPrefetch == 1) {
-        u4 kA[NL], vA[NL], kB[NL], vB[NL];
-        load_tile(t, kA, vA);
+        u4 kB[NL], vB[NL];
+        if (ka != ska || ke != ske) load_tile(t, kA, vA);
         for (; t < t1; t += 8) {
           load_tile(min(t + 4, tlast), kB, vB);
           process(t, kA, vA);
@@ -508,8 +526,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
           process(t + 4, kB, vB);
         }
       } else {
-        u4 kA[NL], vA[NL], kB[NL], vB[NL], kC[NL], vC[NL];
-        load_tile(t, kA, vA);
+        u4 kB[NL], vB[NL], kC[NL], vC[NL];
+        if (ka != ska || ke != ske) load_tile(t, kA, vA);
         load_tile(min(t + 4, tlast), kB, vB);
         for (; t < t1; t += 12) {
           load_tile(min(t + 8, tlast), kC, vC);
@@ -621,7 +639,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     const float mk = a.part.ml[idx * 2];
     sw[k] = mk;
     sl[k] = a.part.ml[idx * 2 + 1];
-    if (k < p.n_pre) mp = fmaxf(mp, mk);
+    if (slice_is_pre(p, k)) mp = fmaxf(mp, mk);
     else mq = fmaxf(mq, mk);
   }
   mp = wave_max(mp);
@@ -637,7 +655,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   // ---- weights: prefix slices relative to Mpre, tail slices to Mall
   float lp = 0.f, lq = 0.f;
   for (int k = tid; k < npart; k += 256) {
-    const bool pre = k < p.n_pre;
+    const bool pre = slice_is_pre(p, k);
     const float mk = sw[k];
     const float w = mk == neg_inf() ? 0.f : exp2f(mk - (pre ? Mpre : Mall));
     sw[k] = w;
@@ -676,7 +694,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
       const int k = k0 + u * NSUB;
       if (k < npart) {
         const float w = sw[k];
-        if (k < p.n_pre) {
+        if (slice_is_pre(p, k)) {
           op.x += w * v[u].x; op.y += w * v[u].y; op.z += w * v[u].z; op.w += w * v[u].w;
         } else {
           oq.x += w * v[u].x; oq.y += w * v[u].y; oq.z += w * v[u].z; oq.w += w * v[u].w;

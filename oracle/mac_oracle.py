@@ -19,7 +19,7 @@ states the three stages only in words:
 * on a miss the step is ordinary full decode attention; on a hit its cost does
   not depend on the context length.
 
-Everything else is a reading, fixed here and listed in the design doc:
+Everything else is a reading of that text, fixed here:
 
 D1  each decode step first appends its token's key/value at index n-1, then
     the query at position n-1 attends to keys [0, n) (itself included).

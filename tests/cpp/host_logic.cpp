@@ -60,18 +60,29 @@ void check_plan(int lo, int n, int band, int S) {
   CHECK(p.n_pre + p.n_post <= S, "too many slices %d + %d > %d", p.n_pre, p.n_post, S);
   CHECK((p.lo < p.mid) == (p.n_pre > 0), "pre slices %d for [%d, %d)", p.n_pre, p.lo, p.mid);
   CHECK((p.mid < p.hi) == (p.n_post > 0), "post slices %d for [%d, %d)", p.n_post, p.mid, p.hi);
+  // walk the slices in key order: pre slices (indices n_post ..), then post
+  // slices (indices 0 .. n_post - 1)
   int cur = p.lo;
-  for (int i = 0; i < p.n_pre + p.n_post; ++i) {
+  for (int q = 0; q < p.n_pre + p.n_post; ++q) {
+    const int i = q < p.n_pre ? p.n_post + q : q - p.n_pre;
     int a, e;
     mac::slice_range(p, i, &a, &e);
-    if (i == p.n_pre) CHECK(cur == p.mid, "pre slices end at %d, not mid %d", cur, p.mid);
+    CHECK(mac::slice_is_pre(p, i) == (q < p.n_pre), "slice %d classified wrongly", i);
+    if (q == p.n_pre) CHECK(cur == p.mid, "pre slices end at %d, not mid %d", cur, p.mid);
     CHECK(a == cur, "slice %d starts at %d, expected %d (lo %d n %d B %d S %d)", i, a, cur, lo, n, band, S);
     CHECK(e > a, "slice %d empty [%d, %d) (lo %d n %d B %d S %d)", i, a, e, lo, n, band, S);
-    if (i < p.n_pre) CHECK(e <= p.mid, "pre slice passes mid");
+    if (q < p.n_pre) CHECK(e <= p.mid, "pre slice passes mid");
     else CHECK(a >= p.mid, "post slice before mid");
-    bool interior_end = (i != p.n_pre - 1) && (i != p.n_pre + p.n_post - 1);
+    bool interior_end = (q != p.n_pre - 1) && (q != p.n_pre + p.n_post - 1);
     if (interior_end) CHECK(e % 16 == 0, "interior bound %d not on a tile edge", e);
     cur = e;
+  }
+  // the slice holding the last key (the fused append's token)
+  if (p.n_pre + p.n_post > 0) {
+    const int last = p.n_post > 0 ? p.n_post - 1 : p.n_pre + p.n_post - 1;
+    int a, e;
+    mac::slice_range(p, last, &a, &e);
+    CHECK(e == (p.n_post ? p.hi : p.mid), "slice %d does not hold the last key", last);
   }
   CHECK(cur == (p.n_post ? p.hi : p.mid), "slices end at %d", cur);
 }
