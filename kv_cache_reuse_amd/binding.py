@@ -54,6 +54,9 @@ class MacConfig(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime; libmac has to bind to the one torch
+    # uses (same device memory, same streams), so torch is loaded first
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libmac is not built ({LIB_PATH} missing); run "

@@ -181,7 +181,11 @@ __host__ __device__ __forceinline__ Plan make_plan(int lo, int n, int band, int 
 __host__ __device__ __forceinline__ int split_bound(int a, int e, int n, int i) {
   if (i <= 0) return a;
   if (i >= n) return e;
-  int x = a + static_cast<int>((int64_t(e - a) * i) / n);
+  // (e - a) * i / n; in 32 bits when the product fits (a 64-bit division is
+  // a long software sequence on the GPU)
+  const int64_t prod = int64_t(e - a) * i;
+  int x = a + (prod <= INT32_MAX ? static_cast<int>(static_cast<int32_t>(prod) / n)
+                                 : static_cast<int>(prod / n));
   x &= ~(kTile - 1);
   return x > a ? x : a;
 }

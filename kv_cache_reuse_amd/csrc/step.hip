@@ -66,13 +66,26 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += row_ror<1>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, shfl_xor_f(v, off));
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
   return v;
 }
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Wave-wide max and sum, the same value in every lane: DPP within each row
+// of 16 lanes, then the four rows' results read from lanes 0, 16, 32, 48 in
+// a fixed order (no LDS round trip).
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_f(v, off);
-  return v;
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 template <int D>
@@ -89,68 +102,90 @@ struct Shared {
 };
 
 // =========================================================== phase A ====
-// One wave: rotary embedding and ring match of query head h (index hi in the
-// group).  All loads are issued before any value is used.
-template <typename T, int D, typename Mid>
-__device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int b, int h, int hi,
-                                           int lane, int n, int p_new, Mid&& mid) {
-  constexpr int EPL = D / 16;
-  const int bh = b * a.hq + h;
-  const int gi = lane / 16, c = lane % 16;
-  const RingView& R = a.ring;
-  const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
-  const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
-  const int32_t* rpn = R.pn + (size_t)bh * R.slots * 2;
+// One wave matches one query head h (index hi in the group).  The loads do
+// not depend on the sequence length, so they are issued first (match_load)
+// and the length is read while they are in flight; match_compute then
+// rotates the query and picks the best ring entry.  16 lanes share one ring
+// slot, each lane holding D/16 elements of the row; a round covers 64 slots.
+template <typename T, int D>
+struct MatchIn {
+  static constexpr int EPL = D / 16;                       // elements per lane
+  static constexpr int NW = EPL * (int)sizeof(T) / 4;      // dwords per lane
+  uint32_t qw[NW];                          // this lane's piece of q_pre
+  uint32_t rw[kMatchSlotsPerGroup][NW];     // its piece of 16 ring rows
+  int2 pn[kMatchSlotsPerGroup];             // (p, n) of those slots
+  double inv;                               // theta^(-2 lane / D)
+  T q1, q2;                                 // rotate-half pair of this lane
+  int cnt;                                  // ring pushes so far
+};
 
-  // a lane's D/16 elements of one query row as 2, 4 or 8 dwords, one vector
-  // load (rows start 16-byte aligned, so the lane's piece is aligned too)
-  constexpr int NW = EPL * (int)sizeof(T) / 4;
-  auto load_row = [&](const T* src, uint32_t (&w)[NW]) {
-    if constexpr (NW == 2) {
-      const u2 v = *reinterpret_cast<const u2*>(src);
-      w[0] = v.x; w[1] = v.y;
-    } else if constexpr (NW == 4) {
-      const u4 v = *reinterpret_cast<const u4*>(src);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
-      const u4 v0 = reinterpret_cast<const u4*>(src)[0];
-      const u4 v1 = reinterpret_cast<const u4*>(src)[1];
-      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-    }
-  };
-  auto elem = [&](const uint32_t (&w)[NW], int e) -> float {
+// a lane's D/16 elements of one row as 2, 4 or 8 dwords, one vector load
+// (rows start 16-byte aligned, so the lane's piece is aligned too)
+template <typename T, int D>
+__device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[MatchIn<T, D>::NW]) {
+  constexpr int NW = MatchIn<T, D>::NW;
+  if constexpr (NW == 2) {
+    const u2 v = *reinterpret_cast<const u2*>(src);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (NW == 4) {
+    const u4 v = *reinterpret_cast<const u4*>(src);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    const u4 v0 = reinterpret_cast<const u4*>(src)[0];
+    const u4 v1 = reinterpret_cast<const u4*>(src)[1];
+    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  }
+}
+
+// Ring slots s0 + gi + 4u (u < 16) of head bh.  Slot indices are clamped into
+// the ring; slots past W + 1 are dropped by the candidate test.
+template <typename T, int D>
+__device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, int s0,
+                                           MatchIn<T, D>& mi) {
+  const RingView& R = a.ring;
+  const int gi = lane / 16, c = lane % 16;
+  const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
+  const int2* rpn = reinterpret_cast<const int2*>(R.pn) + (size_t)bh * R.slots;
+#pragma unroll
+  for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
+    const int s = s0 + gi + 4 * u;
+    const int sc = s < R.slots ? s : 0;
+    load_row<T, D>(rq + (size_t)sc * D + c * MatchIn<T, D>::EPL, mi.rw[u]);
+    mi.pn[u] = rpn[sc];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, MatchIn<T, D>& mi) {
+  const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
+  const bool rot = lane < D / 2;
+  mi.cnt = a.ring.count[bh];
+  mi.inv = rot ? a.inv_freq[lane] : 0.0;
+  mi.q1 = rot ? q[lane] : T(0);
+  mi.q2 = rot ? q[lane + D / 2] : T(0);
+  load_row<T, D>(q + (lane % 16) * MatchIn<T, D>::EPL, mi.qw);
+  load_slots<T, D>(a, bh, lane, 0, mi);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, int bh, int hi,
+                                              int lane, int n, int p_new, MatchIn<T, D>& mi) {
+  constexpr int EPL = MatchIn<T, D>::EPL;
+  const int gi = lane / 16;
+  const RingView& R = a.ring;
+  auto elem = [&](const uint32_t (&w)[MatchIn<T, D>::NW], int e) -> float {
     if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
     else return __uint_as_float(w[e]);
   };
 
-  const int cnt = R.count[bh];
-  const bool rot = lane < D / 2;
-  const double inv = rot ? a.inv_freq[lane] : 0.0;
-  const T q1 = rot ? q[lane] : T(0);
-  const T q2 = rot ? q[lane + D / 2] : T(0);
-  uint32_t qw[NW];
-  load_row(q + c * EPL, qw);
-  // every slot index is clamped into the ring; slots past W + 1 are dropped
-  // by the candidate test (their age is set to W + 1)
-  uint32_t rw[kMatchSlotsPerGroup][NW];
-  int pe[kMatchSlotsPerGroup];
-#pragma unroll
-  for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
-    const int s = gi + 4 * u;
-    const int sc = s < R.slots ? s : 0;
-    load_row(rq + (size_t)sc * D + c * EPL, rw[u]);
-    pe[u] = rpn[sc * 2];
-  }
-  mid();   // further loads, issued behind the ring's
-
   // rotate-half pairs (i, i + D/2): float64 angle and rotation, result scaled
   // by log2(e)/sqrt(D) so that the attention can use exp2
-  if (rot) {
+  if (lane < D / 2) {
     const int i = lane;
     double sn, cs;
-    sincos(static_cast<double>(n - 1) * inv, &sn, &cs);
-    const double x1 = Elem<T>::to_f(q1), x2 = Elem<T>::to_f(q2);
+    sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
+    const double x1 = Elem<T>::to_f(mi.q1), x2 = Elem<T>::to_f(mi.q2);
     const double sc = kLog2e / sqrt(static_cast<double>(D));
     const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
     const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
@@ -171,38 +206,38 @@ __device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int
 
   // Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
   // candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
-  // smallest squared distance, then smallest k (the newest entry).
+  // smallest squared distance, then smallest k (the newest entry).  The
+  // best entry's (p, n) travel with it, so no load follows the argmin.
+  const int cnt = mi.cnt;
   const int nvalid = cnt < R.window ? cnt : R.window;
+  // slot s is (r - s) mod (W + 1) steps old, r = (cnt - 1) mod (W + 1)
+  const int r = cnt > 0 ? (cnt - 1) % R.slots : R.slots - 1;
   float qv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = elem(qw, e);
+  for (int e = 0; e < EPL; ++e) qv[e] = elem(mi.qw, e);
   float best = __builtin_inff();
-  int bestk = -1;
+  int bestk = -1, bp = 0, bn = -1;
   for (int s0 = 0; s0 < R.slots; s0 += 4 * kMatchSlotsPerGroup) {
-    if (s0 > 0) {        // windows of 64 or more: further rounds of loads
-#pragma unroll
-      for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
-        const int s = s0 + gi + 4 * u;
-        const int sc = s < R.slots ? s : 0;
-        load_row(rq + (size_t)sc * D + c * EPL, rw[u]);
-        pe[u] = rpn[sc * 2];
-      }
-    }
+    if (s0 > 0) load_slots<T, D>(a, bh, lane, s0, mi);   // windows of 64 or more
 #pragma unroll
     for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
+      if (s0 + 4 * u >= R.slots) break;   // the rest of the round is padding
       const int s = s0 + gi + 4 * u;
       float d2 = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float df = qv[e] - elem(rw[u], e);
+        const float df = qv[e] - elem(mi.rw[u], e);
         d2 = fmaf(df, df, d2);
       }
       d2 = row16_sum(d2);
-      const int k = s < R.slots ? (cnt - 1 - s + R.slots) % R.slots : R.slots;
-      const bool cand = k < nvalid && pe[u] >= 0 && pe[u] <= p_new && d2 == d2;
+      const int k = s >= R.slots ? R.slots : (r >= s ? r - s : r - s + R.slots);
+      const int pe = mi.pn[u].x;
+      const bool cand = k < nvalid && pe >= 0 && pe <= p_new && d2 == d2;
       if (cand && (d2 < best || (d2 == best && k < bestk))) {
         best = d2;
         bestk = k;
+        bp = pe;
+        bn = mi.pn[u].y;
       }
     }
   }
@@ -210,9 +245,13 @@ __device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int
   for (int off = 16; off <= 32; off <<= 1) {
     const float ob = shfl_xor_f(best, off);
     const int ok = shfl_xor_i(bestk, off);
+    const int op = shfl_xor_i(bp, off);
+    const int on = shfl_xor_i(bn, off);
     if (ok >= 0 && (bestk < 0 || ob < best || (ob == best && ok < bestk))) {
       best = ob;
       bestk = ok;
+      bp = op;
+      bn = on;
     }
   }
   if (lane == 0) {
@@ -220,9 +259,9 @@ __device__ __forceinline__ void match_head(const StepArgs& a, Shared<D>& sh, int
     HeadState hs;
     hs.hit = hit ? 1 : 0;
     hs.slot = hit ? (cnt - 1 - bestk) % R.slots : -1;
-    hs.s = hit ? rpn[hs.slot * 2] : 0;
+    hs.s = hit ? bp : 0;
     hs.cnt = cnt;
-    hs.match_n = hit ? rpn[hs.slot * 2 + 1] : -1;
+    hs.match_n = hit ? bn : -1;
     hs.dist = bestk >= 0 ? sqrtf(best) : __builtin_inff();
     hs.n = n;
     hs.pad = 0;
@@ -264,6 +303,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   };
 
   // ---------------------------------------------------------------- A ----
+  // the match loads of this wave's first head go out before the length
+  const int bh0 = b * a.hq + kvh * G + wave;
+  MatchIn<T, D> mi;
+  if (wave < G) match_load<T, D>(a, bh0, lane, mi);
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
@@ -278,11 +321,25 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   int tspec = st0 + wave < st1 ? st0 + wave : st1 - 1;
   if (tspec < 0) tspec = 0;
   u4 kA[NL], vA[NL];
-  auto spec = [&] { load_tile(tspec, kA, vA); };
-  if (wave < G) match_head<T, D>(a, sh, b, kvh * G + wave, wave, lane, n, p_new, spec);
-  else spec();
-  for (int hi = wave + 4; hi < G; hi += 4)
-    match_head<T, D>(a, sh, b, kvh * G + hi, hi, lane, n, p_new, [] {});
+  load_tile(tspec, kA, vA);
+  // n_post does not depend on the match either: the workgroup of the last
+  // slice after p_new, which holds the new token, stages it in LDS now
+  T* pk = reinterpret_cast<T*>(sh.patch);
+  T* pv = pk + D;
+  const bool early_patch = append && ps.n_post > 0 && slice == ps.n_post - 1;
+  if (early_patch) {
+    const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
+    const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
+    for (int e = tid; e < D; e += 256) {
+      pk[e] = kn[e];
+      pv[e] = vn[e];
+    }
+  }
+  if (wave < G) match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi);
+  for (int hi = wave + 4; hi < G; hi += 4) {
+    match_load<T, D>(a, bh0 + (hi - wave), lane, mi);
+    match_compute<T, D>(a, sh, bh0 + (hi - wave), hi, lane, n, p_new, mi);
+  }
   __syncthreads();
   int lo = sh.head[0].s, smax = sh.head[0].s;
   for (int i = 1; i < G; ++i) {
@@ -339,25 +396,26 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     const bool patcher = append && slice == (p.n_post > 0 ? p.n_post - 1 : nact - 1);
     const int tnew = (n - 1) / kTile, rnew = (n - 1) % kTile;
     // the new token's key and value are staged in LDS (not registers, which
-    // would stay live through the whole tile loop)
-    T* pk = reinterpret_cast<T*>(sh.patch);
-    T* pv = pk + D;
+    // would stay live through the whole tile loop); with slices after p_new
+    // that happened during the match, else (B = 0) it happens here
     if (patcher) {
-      const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
-      const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
-      for (int e = tid; e < D; e += 256) {
-        pk[e] = kn[e];
-        pv[e] = vn[e];
+      if (!early_patch) {
+        const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
+        const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
+        for (int e = tid; e < D; e += 256) {
+          pk[e] = kn[e];
+          pv[e] = vn[e];
+        }
+        __syncthreads();
       }
-      __syncthreads();
       if (wave == 0) {
         const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
         if (base >= 0) {
           T* kw = const_cast<T*>(kc);
           T* vw = const_cast<T*>(vc);
           for (int e = lane; e < D; e += 64) {
-            kw[base + k_tile_offset<T>(rnew, e)] = kn[e];
-            vw[base + v_tile_offset<T>(rnew, e)] = vn[e];
+            kw[base + k_tile_offset<T>(rnew, e)] = pk[e];
+            vw[base + v_tile_offset<T>(rnew, e)] = pv[e];
           }
         }
       }
@@ -581,28 +639,30 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 // ========================================================= merge kernel ==
 // One 256-thread workgroup per query head (b, h): log-sum-exp merge of the
 // reused state and the group's slices, the head's new ring entry and its
-// output.  The m and l of every slice are loaded in one round trip and turned
-// into weights in LDS; thread (sub, quad) then folds every NSUB-th slice's
-// 4 consecutive output dims with 16-byte loads.  All reductions run in a
-// fixed order, so results are bitwise reproducible.
+// output.  Two rounds of loads: the group's match results together with
+// every slice's (m, l) and this thread's first slice outputs (slices the
+// plan does not use hold stale values: they are read in bounds and never
+// enter the arithmetic), then the reused ring state, whose latency hides
+// behind the slice reductions: it joins as one last two-way merge.  Thread
+// (sub, quad) folds every NSUB-th slice's 4 consecutive output dims with
+// 16-byte loads.  All reductions run in a fixed order, so results are
+// bitwise reproducible.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   constexpr int NQ4 = D / 4;            // float4 quads of one head's output
   constexpr int NSUB = 256 / NQ4;       // slice subsets folded in parallel
   constexpr int kBatch = 8;             // loads in flight per thread per round
+  constexpr int kMl = kMaxSlices / 256; // (m, l) loads per thread
   const int bh = blockIdx.x;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group, kvh = h / G, hi = h % G;
   const int S = a.part.S, grp = b * a.hkv + kvh;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int sub = tid / NQ4, d4 = tid % NQ4;
   const RingView& R = a.ring;
   const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
-  const HeadState hs = hsg[hi];
-  const int n = hs.n;
-  int lo = hsg[0].s;
-  for (int i = 1; i < G; ++i) lo = min(lo, hsg[i].s);
-  const Plan p = make_plan(lo, n, a.band, S);
-  const int npart = p.n_pre + p.n_post;
+  const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
+  const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
 
   __shared__ float sw[kMaxSlices];
   __shared__ float sl[kMaxSlices];
@@ -610,37 +670,51 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   __shared__ float4 rp[NSUB][NQ4];
   __shared__ float4 rq[NSUB][NQ4];
 
-  // reused state: the ring stores natural-log m and normalized o
-  float mr = neg_inf(), lr = 0.f;
-  size_t re = 0;
-  if (hs.hit) {
-    re = (size_t)bh * R.slots + hs.slot;
-    const float mn = R.ml[re * 2];
-    lr = R.ml[re * 2 + 1];
-    mr = mn == neg_inf() ? neg_inf() : mn * static_cast<float>(kLog2e);
+  // ---- round 1 (with the query the new ring entry copies)
+  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + 4 * d4;
+  T qv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qv[e] = qsrc[e];
+  const HeadState hs = hsg[hi];
+  int lo = hsg[0].s;
+  for (int i = 1; i < G; ++i) lo = min(lo, hsg[i].s);
+  float2 mlk[kMl];
+#pragma unroll
+  for (int u = 0; u < kMl; ++u) {
+    const int k = tid + 256 * u;
+    if (k < S) mlk[u] = pml[pbase + (size_t)k * G];
   }
-
-  // ---- the first kBatch slices' outputs of this thread are loaded together
-  // with every slice's m and l (one round trip for both)
-  const int sub = tid / NQ4, d4 = tid % NQ4;
   float4 v0[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
-    const int k = sub + u * NSUB;
-    const size_t idx = ((size_t)grp * S + k) * G + hi;
-    v0[u] = k < npart ? reinterpret_cast<const float4*>(a.part.o + idx * D)[d4]
-                      : float4{0.f, 0.f, 0.f, 0.f};
+    const int k = min(sub + u * NSUB, S - 1);
+    v0[u] = reinterpret_cast<const float4*>(a.part.o + (pbase + (size_t)k * G) * D)[d4];
+  }
+  const int n = hs.n;
+  const Plan p = make_plan(lo, n, a.band, S);
+  const int npart = p.n_pre + p.n_post;
+
+  // ---- round 2: the reused state (the ring stores natural-log m and
+  // normalized o)
+  float2 rml = {neg_inf(), 0.f};
+  float4 ro = {0.f, 0.f, 0.f, 0.f};
+  const size_t re = (size_t)bh * R.slots + (hs.hit ? hs.slot : 0);
+  if (hs.hit) {
+    rml = reinterpret_cast<const float2*>(R.ml)[re];
+    ro = reinterpret_cast<const float4*>(R.o + re * D)[d4];
   }
 
-  // ---- m, l of every slice; maxima of the prefix and the tail slices
+  // ---- maxima of the slices before and after p_new
   float mp = neg_inf(), mq = neg_inf();
-  for (int k = tid; k < npart; k += 256) {
-    const size_t idx = ((size_t)grp * S + k) * G + hi;
-    const float mk = a.part.ml[idx * 2];
-    sw[k] = mk;
-    sl[k] = a.part.ml[idx * 2 + 1];
-    if (slice_is_pre(p, k)) mp = fmaxf(mp, mk);
-    else mq = fmaxf(mq, mk);
+#pragma unroll
+  for (int u = 0; u < kMl; ++u) {
+    const int k = tid + 256 * u;
+    if (k < npart) {
+      sw[k] = mlk[u].x;
+      sl[k] = mlk[u].y;
+      if (slice_is_pre(p, k)) mp = fmaxf(mp, mlk[u].x);
+      else mq = fmaxf(mq, mlk[u].x);
+    }
   }
   mp = wave_max(mp);
   mq = wave_max(mq);
@@ -649,15 +723,15 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     red[1][wave] = mq;
   }
   __syncthreads();
-  const float Mpre = fmaxf(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])), mr);
-  const float Mall = fmaxf(Mpre, fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+  const float MA = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  const float MC = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
 
-  // ---- weights: prefix slices relative to Mpre, tail slices to Mall
+  // ---- weights relative to each side's own maximum
   float lp = 0.f, lq = 0.f;
   for (int k = tid; k < npart; k += 256) {
     const bool pre = slice_is_pre(p, k);
     const float mk = sw[k];
-    const float w = mk == neg_inf() ? 0.f : exp2f(mk - (pre ? Mpre : Mall));
+    const float w = mk == neg_inf() ? 0.f : exp2f(mk - (pre ? MA : MC));
     sw[k] = w;
     if (pre) lp += w * sl[k];
     else lq += w * sl[k];
@@ -669,11 +743,10 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     red[3][wave] = lq;
   }
   __syncthreads();
-  const float wr = (hs.hit && mr != neg_inf()) ? exp2f(mr - Mpre) : 0.f;
-  const float Lpre = ((red[2][0] + red[2][1]) + (red[2][2] + red[2][3])) + wr * lr;
-  const float Lpost = (red[3][0] + red[3][1]) + (red[3][2] + red[3][3]);
+  const float LA = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+  const float LC = (red[3][0] + red[3][1]) + (red[3][2] + red[3][3]);
 
-  // ---- o
+  // ---- o of both sides (unnormalized, relative to MA and MC)
   float4 op = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = sub; k0 < npart; k0 += NSUB * kBatch) {
     float4 v[kBatch];
@@ -683,10 +756,8 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     } else {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int k = k0 + u * NSUB;
-        const size_t idx = ((size_t)grp * S + k) * G + hi;
-        v[u] = k < npart ? reinterpret_cast<const float4*>(a.part.o + idx * D)[d4]
-                         : float4{0.f, 0.f, 0.f, 0.f};
+        const int k = min(k0 + u * NSUB, S - 1);
+        v[u] = reinterpret_cast<const float4*>(a.part.o + (pbase + (size_t)k * G) * D)[d4];
       }
     }
 #pragma unroll
@@ -706,38 +777,45 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   rq[sub][d4] = oq;
   __syncthreads();
   if (sub != 0) return;
-  float4 po = {0.f, 0.f, 0.f, 0.f}, qo = {0.f, 0.f, 0.f, 0.f};
+  float4 oa = {0.f, 0.f, 0.f, 0.f}, oc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    po.x += rp[s][d4].x; po.y += rp[s][d4].y; po.z += rp[s][d4].z; po.w += rp[s][d4].w;
-    qo.x += rq[s][d4].x; qo.y += rq[s][d4].y; qo.z += rq[s][d4].z; qo.w += rq[s][d4].w;
+    oa.x += rp[s][d4].x; oa.y += rp[s][d4].y; oa.z += rp[s][d4].z; oa.w += rp[s][d4].w;
+    oc.x += rq[s][d4].x; oc.y += rq[s][d4].y; oc.z += rq[s][d4].z; oc.w += rq[s][d4].w;
   }
-  if (hs.hit) {
-    const float4 ro = reinterpret_cast<const float4*>(R.o + re * D)[d4];
-    const float f = wr * lr;
-    po.x += f * ro.x; po.y += f * ro.y; po.z += f * ro.z; po.w += f * ro.w;
-  }
+
+  // ---- prefix = merge(reused, A), base 2
+  const float mr = (hs.hit && rml.x != neg_inf()) ? rml.x * static_cast<float>(kLog2e) : neg_inf();
+  const float lr = hs.hit ? rml.y : 0.f;
+  const float MP = fmaxf(mr, MA);
+  const float sr = mr == neg_inf() ? 0.f : exp2f(mr - MP);
+  const float sa = MA == neg_inf() ? 0.f : exp2f(MA - MP);
+  const float LP = sr * lr + sa * LA;
+  const float fr = sr * lr;
+  const float4 po = {fr * ro.x + sa * oa.x, fr * ro.y + sa * oa.y,
+                     fr * ro.z + sa * oa.z, fr * ro.w + sa * oa.w};
 
   // ---- the head's new ring entry: (q_pre, prefix state, p_new, n)
   const size_t we = (size_t)bh * R.slots + hs.cnt % R.slots;
-  const float4 eo = Lpre == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
-                                : float4{po.x / Lpre, po.y / Lpre, po.z / Lpre, po.w / Lpre};
+  const float4 eo = LP == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
+                              : float4{po.x / LP, po.y / LP, po.z / LP, po.w / LP};
   reinterpret_cast<float4*>(R.o + we * D)[d4] = eo;
-  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + 4 * d4;
   T* qdst = static_cast<T*>(R.q) + we * D + 4 * d4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) qdst[e] = qsrc[e];
+  for (int e = 0; e < 4; ++e) qdst[e] = qv[e];
 
-  // ---- out = merge(prefix, tail slices)
-  const float sc = Mpre == neg_inf() ? 0.f : exp2f(Mpre - Mall);
-  const float den = Lpre * sc + Lpost;
+  // ---- out = merge(prefix, C)
+  const float M = fmaxf(MP, MC);
+  const float sp = MP == neg_inf() ? 0.f : exp2f(MP - M);
+  const float sc = MC == neg_inf() ? 0.f : exp2f(MC - M);
+  const float den = sp * LP + sc * LC;
   const float4 o4 = den == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
-                               : float4{(po.x * sc + qo.x) / den, (po.y * sc + qo.y) / den,
-                                        (po.z * sc + qo.z) / den, (po.w * sc + qo.w) / den};
+                               : float4{(sp * po.x + sc * oc.x) / den, (sp * po.y + sc * oc.y) / den,
+                                        (sp * po.z + sc * oc.z) / den, (sp * po.w + sc * oc.w) / den};
   reinterpret_cast<float4*>(a.out + (size_t)bh * D)[d4] = o4;
   if (d4 == 0) {
-    R.ml[we * 2] = Lpre == 0.f ? neg_inf() : Mpre * kLn2;
-    R.ml[we * 2 + 1] = Lpre;
+    R.ml[we * 2] = LP == 0.f ? neg_inf() : MP * kLn2;
+    R.ml[we * 2 + 1] = LP;
     R.pn[we * 2] = p.mid;
     R.pn[we * 2 + 1] = n;
     R.count[bh] = hs.cnt + 1;
