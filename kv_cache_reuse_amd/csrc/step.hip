@@ -115,9 +115,17 @@ struct MatchIn {
   uint32_t rw[kMatchSlotsPerGroup][NW];     // its piece of 16 ring rows
   int2 pn[kMatchSlotsPerGroup];             // (p, n) of those slots
   double inv;                               // theta^(-2 lane / D)
-  T q1, q2;                                 // rotate-half pair of this lane
+  // rotate-half pair of this lane, widened to 32 bits: two 16-bit values
+  // sharing a register would have to be packed, which waits for both loads
+  uint32_t q1, q2;
   int cnt;                                  // ring pushes so far
 };
+
+__device__ __forceinline__ uint32_t bits_of(uint16_t x) { return x; }
+__device__ __forceinline__ uint32_t bits_of(float x) { return __float_as_uint(x); }
+template <typename T> __device__ __forceinline__ float from_bits(uint32_t w);
+template <> __device__ __forceinline__ float from_bits<uint16_t>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t w) { return __uint_as_float(w); }
 
 // a lane's D/16 elements of one row as 2, 4 or 8 dwords, one vector load
 // (rows start 16-byte aligned, so the lane's piece is aligned too)
@@ -162,8 +170,8 @@ __device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, 
   const bool rot = lane < D / 2;
   mi.cnt = a.ring.count[bh];
   mi.inv = rot ? a.inv_freq[lane] : 0.0;
-  mi.q1 = rot ? q[lane] : T(0);
-  mi.q2 = rot ? q[lane + D / 2] : T(0);
+  mi.q1 = rot ? bits_of(q[lane]) : 0u;
+  mi.q2 = rot ? bits_of(q[lane + D / 2]) : 0u;
   load_row<T, D>(q + (lane % 16) * MatchIn<T, D>::EPL, mi.qw);
   load_slots<T, D>(a, bh, lane, 0, mi);
 }
@@ -185,7 +193,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
     const int i = lane;
     double sn, cs;
     sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
-    const double x1 = Elem<T>::to_f(mi.q1), x2 = Elem<T>::to_f(mi.q2);
+    const double x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
     const double sc = kLog2e / sqrt(static_cast<double>(D));
     const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
     const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
@@ -217,8 +225,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
   for (int e = 0; e < EPL; ++e) qv[e] = elem(mi.qw, e);
   float best = __builtin_inff();
   int bestk = -1, bp = 0, bn = -1;
-  for (int s0 = 0; s0 < R.slots; s0 += 4 * kMatchSlotsPerGroup) {
-    if (s0 > 0) load_slots<T, D>(a, bh, lane, s0, mi);   // windows of 64 or more
+  auto round = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
       if (s0 + 4 * u >= R.slots) break;   // the rest of the round is padding
@@ -240,6 +247,20 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
         bn = mi.pn[u].y;
       }
     }
+  };
+  // the first round straight-line: a loop header here would merge the
+  // pending-load state and wait for every load in flight, the first tile's
+  // included
+  // (the second round too, for windows of 64 .. 127; a loop takes the rest)
+  constexpr int kRound = 4 * kMatchSlotsPerGroup;
+  round(0);
+  if (R.slots > kRound) {
+    load_slots<T, D>(a, bh, lane, kRound, mi);
+    round(kRound);
+  }
+  for (int s0 = 2 * kRound; s0 < R.slots; s0 += kRound) {
+    load_slots<T, D>(a, bh, lane, s0, mi);
+    round(s0);
   }
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
@@ -304,9 +325,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 
   // ---------------------------------------------------------------- A ----
   // the match loads of this wave's first head go out before the length
-  const int bh0 = b * a.hq + kvh * G + wave;
+  // (waves past the group's heads load a valid head's rows and ignore them:
+  // no branch, so the compiler need not wait for the loads at a join)
+  const int bh0 = b * a.hq + kvh * G + (wave < G ? wave : 0);
   MatchIn<T, D> mi;
-  if (wave < G) match_load<T, D>(a, bh0, lane, mi);
+  match_load<T, D>(a, bh0, lane, mi);
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
@@ -324,21 +347,24 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   load_tile(tspec, kA, vA);
   // n_post does not depend on the match either: the workgroup of the last
   // slice after p_new, which holds the new token, stages it in LDS now
+  // (held in registers through the match, written to LDS after it, so no
+  // wait for these loads lands in front of the match)
   T* pk = reinterpret_cast<T*>(sh.patch);
   T* pv = pk + D;
   const bool early_patch = append && ps.n_post > 0 && slice == ps.n_post - 1;
-  if (early_patch) {
-    const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
-    const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
-    for (int e = tid; e < D; e += 256) {
-      pk[e] = kn[e];
-      pv[e] = vn[e];
-    }
+  T pke = T(0), pve = T(0);
+  if (early_patch && tid < D) {
+    pke = static_cast<const T*>(a.k_new)[((size_t)b * a.hkv + kvh) * D + tid];
+    pve = static_cast<const T*>(a.v_new)[((size_t)b * a.hkv + kvh) * D + tid];
   }
   if (wave < G) match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi);
   for (int hi = wave + 4; hi < G; hi += 4) {
     match_load<T, D>(a, bh0 + (hi - wave), lane, mi);
     match_compute<T, D>(a, sh, bh0 + (hi - wave), hi, lane, n, p_new, mi);
+  }
+  if (early_patch && tid < D) {
+    pk[tid] = pke;
+    pv[tid] = pve;
   }
   __syncthreads();
   int lo = sh.head[0].s, smax = sh.head[0].s;
