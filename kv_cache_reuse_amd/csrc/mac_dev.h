@@ -34,13 +34,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
 }
 
 // Round to nearest, ties to even (IEEE 754 binary32 -> bfloat16); NaN stays
-// a quiet NaN.
+// a NaN.  gfx950 converts in hardware (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+
+// 2^x with one v_exp_f32: results below the smallest normal flush to 0,
+// 2^-inf = 0.  The attention and the merge only take it of x <= 0 or of
+// differences of maxima.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -22,8 +22,9 @@
 //   B. with a non-empty slice: split-K attention on the matrix cores, one
 //      partial state (o, m, l) per head.  Each wave's first tile under the
 //      plan a miss would give is loaded while the match runs, and kept when
-//      the real plan gives the slice the same keys (always on a miss, and for
-//      the slices after p_new on a hit).  With a fused append, the workgroup
+//      the real plan gives the wave the same first tile (always on a miss,
+//      and for the slices after p_new on a hit); for the first slice before
+//      p_new one wave loads the tile a typical hit starts in instead.  With a fused append, the workgroup
 //      whose slice holds the new token stores it in the cache and patches it
 //      into the tile it loads.
 //  merge_kernel, one workgroup per query head: log-sum-exp merge of the
@@ -176,9 +177,13 @@ __device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, 
   load_slots<T, D>(a, bh, lane, 0, mi);
 }
 
+// With write false the wave only consumes its loads (a wave past the
+// group's heads): loads left unread make the compiler wait for every load in
+// flight before their registers are reused.
 template <typename T, int D>
 __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, int bh, int hi,
-                                              int lane, int n, int p_new, MatchIn<T, D>& mi) {
+                                              int lane, int n, int p_new, MatchIn<T, D>& mi,
+                                              bool write = true) {
   constexpr int EPL = MatchIn<T, D>::EPL;
   const int gi = lane / 16;
   const RingView& R = a.ring;
@@ -189,7 +194,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
 
   // rotate-half pairs (i, i + D/2): float64 angle and rotation, result scaled
   // by log2(e)/sqrt(D) so that the attention can use exp2
-  if (lane < D / 2) {
+  if (write && lane < D / 2) {
     const int i = lane;
     double sn, cs;
     sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
@@ -275,7 +280,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
       bn = on;
     }
   }
-  if (lane == 0) {
+  if (write && lane == 0) {
     const bool hit = bestk >= 0 && best < a.tau2;
     HeadState hs;
     hs.hit = hit ? 1 : 0;
@@ -305,7 +310,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int slice = blockIdx.x / n_groups;
   const int b = grp / a.hkv, kvh = grp % a.hkv;
   const int G = a.group;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  // the wave index is the same in every lane of a wave; readfirstlane makes
+  // that visible to the compiler, so per-wave loop bounds and branches are
+  // scalar (vector control flow around loads makes it wait for all of them)
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const bool fused = a.k_new != nullptr;
 
   const T* kc = static_cast<const T*>(a.k_cache);
@@ -336,13 +345,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int p_new = n - a.band > 0 ? n - a.band : 0;
   // The group's plan when any of its heads misses does not depend on the
   // match: this wave's first tile under it is loaded while the match runs
-  // and kept if the real plan gives the slice the same keys.
+  // and kept if the real plan gives the wave the same first tile.
   const Plan ps = make_plan(0, n, a.band, a.part.S);
   int ska = 0, ske = 0;
   if (slice < ps.n_pre + ps.n_post) slice_range(ps, slice, &ska, &ske);
   const int st0 = ska / kTile, st1 = (ske + kTile - 1) / kTile;
   int tspec = st0 + wave < st1 ? st0 + wave : st1 - 1;
   if (tspec < 0) tspec = 0;
+  // On a hit the first slice before p_new usually holds only key p_new - 1
+  // (a match one step old starts its band one key earlier): wave 0 of that
+  // workgroup loads the tile of that key instead.  On a miss it reloads.
+  if (ps.n_pre > 0 && slice == ps.n_post && wave == 0) tspec = (p_new - 1) / kTile;
   u4 kA[NL], vA[NL];
   load_tile(tspec, kA, vA);
   // n_post does not depend on the match either: the workgroup of the last
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     pke = static_cast<const T*>(a.k_new)[((size_t)b * a.hkv + kvh) * D + tid];
     pve = static_cast<const T*>(a.v_new)[((size_t)b * a.hkv + kvh) * D + tid];
   }
-  if (wave < G) match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi);
+  match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi, wave < G);
   for (int hi = wave + 4; hi < G; hi += 4) {
     match_load<T, D>(a, bh0 + (hi - wave), lane, mi);
     match_compute<T, D>(a, sh, bh0 + (hi - wave), hi, lane, n, p_new, mi);
@@ -374,12 +387,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   }
   const Plan p = make_plan(lo, n, a.band, a.part.S);
   const int nact = p.n_pre + p.n_post;
-  if (slice == 0 && tid < G) {
-    const int bh = b * a.hq + kvh * G + tid;
-    a.heads[bh] = sh.head[tid];
-    if (a.match_ctx_out) a.match_ctx_out[bh] = sh.head[tid].match_n;
-    if (a.dist_out) a.dist_out[bh] = sh.head[tid].dist;
-  }
 
   // ---------------------------------------------------------------- B ----
   if (slice < nact) {
@@ -424,27 +431,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     // the new token's key and value are staged in LDS (not registers, which
     // would stay live through the whole tile loop); with slices after p_new
     // that happened during the match, else (B = 0) it happens here
-    if (patcher) {
-      if (!early_patch) {
-        const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
-        const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
-        for (int e = tid; e < D; e += 256) {
-          pk[e] = kn[e];
-          pv[e] = vn[e];
-        }
-        __syncthreads();
+    if (patcher && !early_patch) {
+      const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
+      const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
+      for (int e = tid; e < D; e += 256) {
+        pk[e] = kn[e];
+        pv[e] = vn[e];
       }
-      if (wave == 0) {
-        const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
-        if (base >= 0) {
-          T* kw = const_cast<T*>(kc);
-          T* vw = const_cast<T*>(vc);
-          for (int e = lane; e < D; e += 64) {
-            kw[base + k_tile_offset<T>(rnew, e)] = pk[e];
-            vw[base + v_tile_offset<T>(rnew, e)] = pv[e];
-          }
-        }
-      }
+      __syncthreads();
     }
 
     v4f acc[NCT];
@@ -546,7 +540,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
       const float mnew = fmaxf(m, mx);
       if (mnew > m) {
-        const float alpha = exp2f(m - mnew);
+        const float alpha = fast_exp2(m - mnew);
 #pragma unroll
         for (int i = 0; i < NCT; ++i) acc[i] *= alpha;
         lsum *= alpha;
@@ -556,7 +550,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = exp2f(s[r] - mref);
+        pr[r] = fast_exp2(s[r] - mref);
         lsum += pr[r];
       }
 
@@ -596,37 +590,60 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     // cache hit): a load under a branch leaves the outstanding-load count
     // unknown at the join, and the compiler then waits for every load,
     // prefetches included, before the current tile's math.
+    // nt tiles for this wave: t0 + wave, + 4, ...; pairs in a loop with one
+    // exit (a loop left in the middle makes the compiler wait for every
+    // load in flight at its header), then the odd one
     const int tlast = t1 - 1;
-    int t = t0 + wave;
-    if (t < t1) {
+    const int tw = t0 + wave;
+    const int nt = tw < t1 ? (t1 - tw + 3) / 4 : 0;
+    if (nt > 0) {
       if constexpr (kPrefetch == 1) {
         u4 kB[NL], vB[NL];
-        if (ka != ska || ke != ske) load_tile(t, kA, vA);
-        for (; t < t1; t += 8) {
-          load_tile(min(t + 4, tlast), kB, vB);
+        if (tw != tspec) load_tile(tw, kA, vA);
+        int i = 0;
+        for (; i + 1 < nt; i += 2) {
+          const int t = tw + 4 * i;
+          load_tile(t + 4, kB, vB);
           process(t, kA, vA);
-          if (t + 4 >= t1) break;
           load_tile(min(t + 8, tlast), kA, vA);
           process(t + 4, kB, vB);
         }
+        if (i < nt) process(tw + 4 * i, kA, vA);
       } else {
         u4 kB[NL], vB[NL], kC[NL], vC[NL];
-        if (ka != ska || ke != ske) load_tile(t, kA, vA);
-        load_tile(min(t + 4, tlast), kB, vB);
-        for (; t < t1; t += 12) {
-          load_tile(min(t + 8, tlast), kC, vC);
+        if (tw != tspec) load_tile(tw, kA, vA);
+        load_tile(min(tw + 4, tlast), kB, vB);
+        int i = 0;
+        for (; i + 2 < nt; i += 3) {
+          const int t = tw + 4 * i;
+          load_tile(t + 8, kC, vC);
           process(t, kA, vA);
-          if (t + 4 >= t1) break;
           load_tile(min(t + 12, tlast), kA, vA);
           process(t + 4, kB, vB);
-          if (t + 8 >= t1) break;
           load_tile(min(t + 16, tlast), kB, vB);
           process(t + 8, kC, vC);
         }
+        if (i < nt) process(tw + 4 * i, kA, vA);
+        if (i + 1 < nt) process(tw + 4 * i + 4, kB, vB);
       }
     }
     lsum += shfl_xor_f(lsum, 16);
     lsum += shfl_xor_f(lsum, 32);
+
+    // The new token goes into the cache only now: stores count in the same
+    // counter as loads, and one issued before the tile loop would be waited
+    // for at its entry.  No other workgroup reads this slot in this step.
+    if (patcher && wave == 0) {
+      const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
+      if (base >= 0) {
+        T* kw = const_cast<T*>(kc);
+        T* vw = const_cast<T*>(vc);
+        for (int e = lane; e < D; e += 64) {
+          kw[base + k_tile_offset<T>(rnew, e)] = pk[e];
+          vw[base + v_tile_offset<T>(rnew, e)] = pv[e];
+        }
+      }
+    }
 
     // ---- the four waves' states -> the slice's partial state
     if (lg == 0) {
@@ -648,7 +665,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float mw = sh.m[w][hh];
-        const float sc = mw == neg_inf() ? 0.f : exp2f(mw - Mx);
+        const float sc = mw == neg_inf() ? 0.f : fast_exp2(mw - Mx);
         o += sc * sh.o[w][hh][dim];
         L += sc * sh.l[w][hh];
       }
@@ -660,6 +677,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
   }
 
+  // the match results, for the merge kernel and the optional outputs (last,
+  // for the same reason as the token's store)
+  if (slice == 0 && tid < G) {
+    const int bh = b * a.hq + kvh * G + tid;
+    a.heads[bh] = sh.head[tid];
+    if (a.match_ctx_out) a.match_ctx_out[bh] = sh.head[tid].match_n;
+    if (a.dist_out) a.dist_out[bh] = sh.head[tid].dist;
+  }
 }
 
 // ========================================================= merge kernel ==
@@ -683,7 +708,11 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group, kvh = h / G, hi = h % G;
   const int S = a.part.S, grp = b * a.hkv + kvh;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  // the wave index is the same in every lane of a wave; readfirstlane makes
+  // that visible to the compiler, so per-wave loop bounds and branches are
+  // scalar (vector control flow around loads makes it wait for all of them)
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int sub = tid / NQ4, d4 = tid % NQ4;
   const RingView& R = a.ring;
   const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
@@ -757,7 +786,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   for (int k = tid; k < npart; k += 256) {
     const bool pre = slice_is_pre(p, k);
     const float mk = sw[k];
-    const float w = mk == neg_inf() ? 0.f : exp2f(mk - (pre ? MA : MC));
+    const float w = mk == neg_inf() ? 0.f : fast_exp2(mk - (pre ? MA : MC));
     sw[k] = w;
     if (pre) lp += w * sl[k];
     else lq += w * sl[k];
@@ -814,8 +843,8 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   const float mr = (hs.hit && rml.x != neg_inf()) ? rml.x * static_cast<float>(kLog2e) : neg_inf();
   const float lr = hs.hit ? rml.y : 0.f;
   const float MP = fmaxf(mr, MA);
-  const float sr = mr == neg_inf() ? 0.f : exp2f(mr - MP);
-  const float sa = MA == neg_inf() ? 0.f : exp2f(MA - MP);
+  const float sr = mr == neg_inf() ? 0.f : fast_exp2(mr - MP);
+  const float sa = MA == neg_inf() ? 0.f : fast_exp2(MA - MP);
   const float LP = sr * lr + sa * LA;
   const float fr = sr * lr;
   const float4 po = {fr * ro.x + sa * oa.x, fr * ro.y + sa * oa.y,
@@ -832,8 +861,8 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
 
   // ---- out = merge(prefix, C)
   const float M = fmaxf(MP, MC);
-  const float sp = MP == neg_inf() ? 0.f : exp2f(MP - M);
-  const float sc = MC == neg_inf() ? 0.f : exp2f(MC - M);
+  const float sp = MP == neg_inf() ? 0.f : fast_exp2(MP - M);
+  const float sc = MC == neg_inf() ? 0.f : fast_exp2(MC - M);
   const float den = sp * LP + sc * LC;
   const float4 o4 = den == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
                                : float4{(sp * po.x + sc * oc.x) / den, (sp * po.y + sc * oc.y) / den,
