@@ -14,9 +14,12 @@ Printed: one JSON line.  `value` is the effective KV bandwidth of the miss
 path (every step misses: jump probability 1), i.e. algorithmic bytes / time;
 `sweep` holds the hit-rate sweep (jump probability 1, 0.5, 0.2, 0.05) with
 us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
-latency at contexts 8K..128K; `roofline` the step kernel's achieved
-bandwidth from HIP events around its launches; `cpu_baseline` the fp64
-oracle timed on a bounded sample of the same workload on the host cores.
+latency at contexts 8K..128K; `latency_classes` per-step p10/p50/p90 at
+jump probability 0.2 split by the step's decisions (every head hit, every
+head missed, mixed); `read_ceiling` the rate of a plain streaming-read
+kernel on the same device; `roofline` the step kernel's achieved bandwidth
+from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
+on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -150,14 +153,16 @@ def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefil
 
 
 def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
-              context=None, prefill_upto=None, inputs_cache=None):
+              context=None, prefill_upto=None, inputs_cache=None, per_step=False):
     """warmup + steps decode steps, round-robin over `layers` layer copies.
 
     The warmup runs eagerly.  With `graph` the timed steps are captured into
     one HIP graph (through torch.cuda.CUDAGraph, on the capture stream) and
     the graph is replayed exactly once inside the timed region; otherwise
     they are launched eagerly.  `kernel_timing` (eager only) brackets every
-    split-K attention launch with HIP events on the step's stream."""
+    split-K attention launch with HIP events on the step's stream.  With
+    `per_step` (eager) every step is bracketed by events too and the
+    durations come back as the fifth value."""
     import torch
     from kv_cache_reuse_amd import binding as B
     per_layer = (steps + warmup + layers - 1) // layers + 1
@@ -168,7 +173,7 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
         Ls[i].step()
     torch.cuda.synchronize()
     starts = [L.t for L in Ls]
-    use_graph = graph and not kernel_timing
+    use_graph = graph and not kernel_timing and not per_step
     g = None
     if use_graph:
         g = torch.cuda.CUDAGraph()
@@ -183,15 +188,25 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    marks = []
     e0.record(stream)
     if use_graph:
         g.replay()
     else:
         for i in order[warmup:]:
-            Ls[i].step()
+            if per_step:
+                ea = torch.cuda.Event(enable_timing=True)
+                eb = torch.cuda.Event(enable_timing=True)
+                ea.record(stream)
+                Ls[i].step()
+                eb.record(stream)
+                marks.append((i, Ls[i].t - 1, ea, eb))
+            else:
+                Ls[i].step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    step_us = [(i, t, 1e3 * ea.elapsed_time(eb)) for i, t, ea, eb in marks]
     kms, klaunch = 0.0, 0
     if kernel_timing:
         for L in Ls:
@@ -200,18 +215,75 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
             klaunch += n
             B.mac_profile_enable(L.sess.ctx, False)
     recs = []
+    mns = []
     for li, L in enumerate(Ls):
         mn = L.match_n[:L.t].cpu().numpy()
+        mns.append(mn)
         for t in range(starts[li], L.t):
             n_ctx = L.inp.contexts + t + 1
             cnt = np.full((w.batch, w.n_q_heads), min(t, w.window))
             recs.append((n_ctx, mn[t], cnt))
+    classes = [(("all_hit" if (mns[i][t] >= 0).all() else
+                 "all_miss" if (mns[i][t] < 0).all() else "mixed"), us)
+               for i, t, us in step_us]
     del g
     for L in Ls:
         L.sess.close()
     del Ls
     torch.cuda.empty_cache()
+    if per_step:
+        return ms, recs, kms, klaunch, classes
     return ms, recs, kms, klaunch
+
+
+def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache):
+    """Per-step latency (HIP events around each eager step) by the step's
+    decisions: every head hit, every head missed, or mixed."""
+    out = run_point(w, p_jump, steps, warmup, layers, graph=False, inputs_cache=inputs_cache,
+                    per_step=True)
+    res = {}
+    for cls in ("all_hit", "mixed", "all_miss"):
+        v = np.array([us for c, us in out[4] if c == cls])
+        if len(v):
+            res[cls] = {"steps": int(len(v)), "p10_us": float(np.percentile(v, 10)),
+                        "p50_us": float(np.percentile(v, 50)),
+                        "p90_us": float(np.percentile(v, 90))}
+    return res
+
+
+def read_ceiling():
+    """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
+    2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
+    each timed with HIP events."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_reuse_amd", "libmac_bw.so"))
+    lib.mac_bw_read.restype = ctypes.c_int
+    lib.mac_bw_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = (0.0, 0)
+    for blocks in (512, 1024, 2048, 4096, 8192, 16384):
+        for rep_ in range(4):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.mac_bw_read(buf.data_ptr(), nbytes, sink.data_ptr(), 0x9e3779b9, blocks,
+                                 stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"mac_bw_read failed with HIP error {st}")
+            if rep_ > 0:
+                gbps = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+                best = max(best, (gbps, blocks))
+    del buf
+    torch.cuda.empty_cache()
+    return {"GBps": best[0], "blocks": best[1], "bytes": nbytes,
+            "pct_hbm_peak": 100.0 * best[0] / HBM_PEAK_GBPS}
 
 
 def summarize(w, ms, recs, steps):
@@ -304,6 +376,8 @@ def main():
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-flatness", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--points", type=str, default="")
@@ -386,6 +460,23 @@ def main():
     if not args.no_flatness:
         flat_steps = hit_step_latency(w, cache)
 
+    # ---- per-step latency by decision class (eager, events around each step)
+    lat = None
+    if not args.no_latency:
+        log("latency classes: p_jump=0.2, eager per-step events")
+        lat = latency_classes(w, 0.2, args.steps, args.warmup, args.layers, cache)
+        for k, v in lat.items():
+            log(f"  {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / {v['p50_us']:.1f} / "
+                f"{v['p90_us']:.1f} us")
+
+    # ---- streaming-read ceiling of this device, same run
+    ceil = None
+    if not args.no_ceiling:
+        ceil = read_ceiling()
+        roofline["pct_of_read_ceiling"] = 100.0 * achieved / ceil["GBps"]
+        log(f"read ceiling: {ceil['GBps']:.0f} GB/s ({ceil['pct_hbm_peak']:.1f} % of peak); "
+            f"step kernel at {roofline['pct_of_read_ceiling']:.1f} % of it")
+
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle, {args.cpu_steps} steps")
@@ -416,6 +507,8 @@ def main():
         "pct_hbm_peak": head["pct_hbm_peak"],
         "sweep": sweep,
         "flatness": flat_steps,
+        "latency_classes": lat,
+        "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -1,6 +1,9 @@
-"""Build libmac.so in-tree for gfx950 with hipcc.
+"""Build the libraries in-tree for gfx950 with hipcc.
 
     python -m kv_cache_reuse_amd.build
+
+libmac.so is the decode path (C ABI in include/mac.h); libmac_bw.so is the
+streaming-read probe the benchmark measures the bandwidth ceiling with.
 """
 
 import os
@@ -8,20 +11,30 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/step.hip", "csrc/kv_ring.hip", "csrc/mac_api.hip"]
+LIBS = {
+    "libmac.so": ["csrc/step.hip", "csrc/kv_ring.hip", "csrc/mac_api.hip"],
+    "libmac_bw.so": ["csrc/bw_probe.hip"],
+}
+SOURCES = LIBS["libmac.so"]
 OUT = os.path.join(HERE, "libmac.so")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
-    # keep the compiler from forming packed fp32 ops (see the design notes)
+    # the compiler must not form packed fp32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
 
 def build(verbose: bool = False) -> str:
+    for name, sources in LIBS.items():
+        _build_one(os.path.join(HERE, name), sources, verbose)
+    return OUT
+
+
+def _build_one(out: str, sources, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc, *FLAGS, "-o", tmp, *[os.path.join(HERE, s) for s in SOURCES]]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, "-o", tmp, *[os.path.join(HERE, s) for s in sources]]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -32,8 +45,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed with status {r.returncode}")
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
