@@ -206,6 +206,26 @@ mac_status mac_query_cache_push(mac_ctx* ctx, const void* q_pre,
                                 void* stream);
 
 /*
+ * Seed the rings from a prefill (abstract: the match stage looks for
+ * similar queries in a short window of recent ones; with the window read as
+ * the last W decode steps, a fresh prefill leaves it empty and the first
+ * decode steps cannot match).  q_hist is device [n_hist][batch][Hq][d],
+ * config dtype: the pre-RoPE queries of the last n_hist positions of every
+ * sequence (q_hist[j][b] belongs to position seq_lens[b] - n_hist + j).
+ * Each position is replayed, oldest first, as a decode step that does not
+ * match: its query attends to keys [0, position], and the entry it pushes is
+ * the one a miss there would push (exact prefix state over
+ * [0, max(0, position + 1 - B)), p, n = position + 1).  The step's outputs
+ * are discarded (workspace); seq_lens_dev is unchanged afterwards.
+ * 0 <= n_hist <= W and every sequence must hold at least n_hist keys
+ * (MAC_ERR_INVALID_ARG otherwise, before any device call).  Costs n_hist
+ * miss-path steps.
+ */
+mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* page_table, void* stream);
+
+/*
  * Kernel timing for measurement.  While enabled, each mac_decode_step
  * records a pair of HIP events around its split-K attention launch on the
  * step's stream (at most 65536 pairs are kept).  mac_profile_read waits for

@@ -32,7 +32,8 @@ MAC_DTYPE_BF16 = 1
 EXPORTED = (
     "mac_kv_cache_bytes", "mac_ring_bytes", "mac_workspace_bytes", "mac_init",
     "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
-    "mac_decode_step_append", "mac_query_cache_push", "mac_profile_enable", "mac_profile_read",
+    "mac_decode_step_append", "mac_seed_ring", "mac_query_cache_push", "mac_profile_enable",
+    "mac_profile_read",
     "mac_destroy", "mac_last_error",
 )
 
@@ -73,6 +74,7 @@ def _load():
         "mac_read_kv": (c_int, [P, P, P, P, c_int32, c_int32, c_int32, P, P, P]),
         "mac_decode_step": (c_int, [P, P, P, P, P, P, P, P, P]),
         "mac_decode_step_append": (c_int, [P, P, P, P, P, P, P, P, P, P, P]),
+        "mac_seed_ring": (c_int, [P, P, c_int32, P, P, P, P]),
         "mac_query_cache_push": (c_int, [P, P, P, P, P, P, P, P, P]),
         "mac_profile_enable": (c_int, [P, c_int]),
         "mac_profile_read": (c_int, [P, POINTER(c_double), POINTER(c_int64)]),
@@ -150,6 +152,10 @@ def mac_decode_step_append(ctx, q_pre, k_new, v_new, k_cache, v_cache, page_tabl
     _check(_lib.mac_decode_step_append(ctx, q_pre, k_new, v_new, k_cache, v_cache,
                                        page_table or None, out, match_ctx_out or None,
                                        dist_out or None, stream))
+
+
+def mac_seed_ring(ctx, q_hist, n_hist, k_cache, v_cache, page_table, stream):
+    _check(_lib.mac_seed_ring(ctx, q_hist, n_hist, k_cache, v_cache, page_table or None, stream))
 
 
 def mac_query_cache_push(ctx, q_pre, o, m, l, prefix_end, ctx_len, mask, stream):
@@ -282,6 +288,13 @@ class MacSession:
         mac_read_kv(self.ctx, self.k_cache.data_ptr(), self.v_cache.data_ptr(), self._pt(),
                     seq, start, count, k.data_ptr(), v.data_ptr(), self._s())
         return k, v
+
+    def seed(self, q_hist):
+        """q_hist: [n_hist, batch, Hq, d] pre-RoPE queries of the last n_hist
+        positions of every sequence (contiguous, config dtype, on device)."""
+        assert q_hist.is_contiguous() and q_hist.dtype == self.dtype
+        mac_seed_ring(self.ctx, q_hist.data_ptr(), int(q_hist.shape[0]), self.k_cache.data_ptr(),
+                      self.v_cache.data_ptr(), self._pt(), self._s())
 
     def push(self, q_pre, o, m, l, prefix_end, ctx_len, mask=None):
         mac_query_cache_push(self.ctx, q_pre.data_ptr(), o.data_ptr(), m.data_ptr(),

@@ -83,6 +83,16 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Sequence lengths around ring seeding: mode 0 saves them, mode 1 sets each
+// to its saved value plus `offset`, mode 2 restores them.
+__global__ void seed_len_kernel(int32_t* lens, int32_t* saved, int batch, int mode, int offset) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  if (mode == 0) saved[b] = lens[b];
+  else if (mode == 1) lens[b] = saved[b] + offset;
+  else lens[b] = saved[b];
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void push_kernel(RingView R, int hq, const T* q, const float* o,
                                                    const float* m, const float* l, const int32_t* pe,
@@ -149,6 +159,13 @@ hipError_t launch_read(const void* kc, const void* vc, const int32_t* pt, void* 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_seed_len(int32_t* lens, int32_t* saved, int batch, int mode, int offset,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(seed_len_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, lens, saved,
+                     batch, mode, offset);
   return hipGetLastError();
 }
 

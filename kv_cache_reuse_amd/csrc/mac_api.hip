@@ -46,7 +46,7 @@ struct Layout {
   // ring
   size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
   // workspace
-  size_t w_po, w_pml, w_heads, w_invf, ws_bytes;
+  size_t w_po, w_pml, w_heads, w_invf, w_out, w_save, ws_bytes;
   int slices;
   int64_t capacity;     // keys per sequence
   int tiles_per_seq;    // contiguous cache
@@ -126,6 +126,8 @@ Layout layout(const mac_config* c) {
   L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
   L.w_heads = off;   off = align256(off + bh * sizeof(mac::HeadState));
   L.w_invf = off;  off = align256(off + (d / 2) * 8);
+  L.w_out = off;   off = align256(off + bh * d * 4);          // ring seeding: discarded outputs
+  L.w_save = off;  off = align256(off + (size_t)c->batch * 4); // ring seeding: saved lengths
   L.ws_bytes = off;
   return L;
 }
@@ -324,6 +326,39 @@ mac_status mac_read_kv(mac_ctx* ctx, const void* k_cache, const void* v_cache,
 namespace {
 
 // Shared body of mac_decode_step and mac_decode_step_append (k_new != null).
+// Kernel arguments of one step; fused-append and optional outputs unset.
+mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, float* out) {
+  const mac_config& c = ctx->cfg;
+  const Layout& L = ctx->L;
+  mac::StepArgs a;
+  a.q_pre = q_pre;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.seq_lens = ctx->seq_lens_dev;
+  a.inv_freq = reinterpret_cast<const double*>(ctx->ws + L.w_invf);
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.out = out;
+  a.match_ctx_out = nullptr;
+  a.dist_out = nullptr;
+  a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
+  a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
+  a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
+  a.part.S = L.slices;
+  a.ring = ctx->ring_view();
+  a.geom = ctx->geom();
+  a.batch = c.batch;
+  a.hq = c.n_q_heads;
+  a.hkv = c.n_kv_heads;
+  a.group = c.n_q_heads / c.n_kv_heads;
+  a.band = c.band;
+  a.tau2 = static_cast<float>((double)c.tau * (double)c.tau);
+  a.theta = c.rope_theta;
+  return a;
+}
+
 mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, const void* v_cache,
                        const int32_t* page_table, float* out, int32_t* match_ctx_out,
                        float* dist_out, const void* k_new, const void* v_new, void* stream) {
@@ -348,32 +383,11 @@ mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, con
   }
 
   const mac_config& c = ctx->cfg;
-  const Layout& L = ctx->L;
-  mac::StepArgs a;
-  a.q_pre = q_pre;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.page_table = page_table;
-  a.seq_lens = ctx->seq_lens_dev;
-  a.inv_freq = reinterpret_cast<const double*>(ctx->ws + L.w_invf);
+  mac::StepArgs a = step_args(ctx, q_pre, k_cache, v_cache, page_table, out);
   a.k_new = k_new;
   a.v_new = v_new;
-  a.out = out;
   a.match_ctx_out = match_ctx_out;
   a.dist_out = dist_out;
-  a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
-  a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
-  a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
-  a.part.S = L.slices;
-  a.ring = ctx->ring_view();
-  a.geom = ctx->geom();
-  a.batch = c.batch;
-  a.hq = c.n_q_heads;
-  a.hkv = c.n_kv_heads;
-  a.group = c.n_q_heads / c.n_kv_heads;
-  a.band = c.band;
-  a.tau2 = static_cast<float>((double)c.tau * (double)c.tau);
-  a.theta = c.rope_theta;
 
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (ctx->profiling && ctx->ev_used < 65536) {
@@ -416,6 +430,43 @@ mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k
   if (!k_new || !v_new) return fail(MAC_ERR_INVALID_ARG, "k_new and v_new are required");
   return decode_impl(ctx, q_pre, k_cache, v_cache, page_table, out, match_ctx_out, dist_out,
                      k_new, v_new, stream);
+}
+
+mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  const mac_config& c = ctx->cfg;
+  if (n_hist < 0 || n_hist > c.window)
+    return fail(MAC_ERR_INVALID_ARG, "n_hist must be in [0, W = %d] (got %d)", c.window, n_hist);
+  if (n_hist == 0) return ok();
+  if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
+  if ((s = check_ptr(q_hist, "q_hist"))) return s;
+  for (int b = 0; b < c.batch; ++b)
+    if (ctx->mirror[b] < n_hist)
+      return fail(MAC_ERR_INVALID_ARG, "sequence %d holds %lld keys, fewer than the %d positions "
+                  "to seed", b, (long long)ctx->mirror[b], n_hist);
+  // Position N - n_hist + j of every sequence is replayed as a decode step
+  // whose match cannot hit (tau^2 < 0): the step reads the sequence length
+  // as that position + 1, attends over [0, position], and pushes the entry
+  // a miss there would have pushed.  Outputs land in the workspace.
+  const Layout& L = ctx->L;
+  mac::StepArgs a = step_args(ctx, q_hist, k_cache, v_cache, page_table,
+                              reinterpret_cast<float*>(ctx->ws + L.w_out));
+  a.tau2 = -1.0f;
+  int32_t* saved = reinterpret_cast<int32_t*>(ctx->ws + L.w_save);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t q_step = (size_t)c.batch * c.n_q_heads * c.head_dim * elem_size(c.dtype);
+  hipError_t e = mac::launch_seed_len(ctx->seq_lens_dev, saved, c.batch, 0, 0, st);
+  for (int j = 0; j < n_hist && e == hipSuccess; ++j) {
+    e = mac::launch_seed_len(ctx->seq_lens_dev, saved, c.batch, 1, j + 1 - n_hist, st);
+    if (e != hipSuccess) break;
+    a.q_pre = static_cast<const char*>(q_hist) + j * q_step;
+    e = mac::launch_step(a, c.dtype, c.head_dim, c.page_size ? 1 : 0, st, nullptr, nullptr);
+  }
+  if (e == hipSuccess) e = mac::launch_seed_len(ctx->seq_lens_dev, saved, c.batch, 2, 0, st);
+  if (e != hipSuccess) return device_fail(ctx, e, "mac_seed_ring");
+  return ok();
 }
 
 mac_status mac_query_cache_push(mac_ctx* ctx, const void* q_pre, const float* o, const float* m,

@@ -26,6 +26,10 @@ hipError_t launch_read(const void* kc, const void* vc, const int32_t* pt, void* 
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 
+// mode 0: saved = lens; 1: lens = saved + offset; 2: lens = saved
+hipError_t launch_seed_len(int32_t* lens, int32_t* saved, int batch, int mode, int offset,
+                           hipStream_t st);
+
 hipError_t launch_inv_freq(double* out, int d, double theta, hipStream_t st);
 
 hipError_t launch_push(const RingView& R, int batch, int hq, int d, int dtype, const void* q,

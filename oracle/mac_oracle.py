@@ -322,6 +322,24 @@ class MacOracle:
         return res
 
 
+    def seed(self, b: int, q_hist: np.ndarray, K: np.ndarray, V: np.ndarray,
+             n_now: int) -> None:
+        """Ring seeding from a prefill.
+
+        Reading of the match stage's window (MAC-Attention abstract) as the
+        last W decode steps leaves it empty after a prefill.  Seeding replays
+        the last len(q_hist) positions of sequence b, whose cache holds n_now
+        keys, oldest first, as decode steps that do not match: each pushes the
+        entry a miss at that position would push (the exact prefix state of
+        its own query over [0, max(0, position + 1 - B)))."""
+        q_hist = np.asarray(q_hist, dtype=np.float64).reshape(-1, self.hq, self.d)
+        m = q_hist.shape[0]
+        assert 0 <= m <= self.W and m <= n_now
+        no_match = {h: (False, -1) for h in range(self.hq)}
+        for j in range(m):
+            self.step(b, q_hist[j], K, V, n_now - m + j + 1, force=no_match)
+
+
 # ---------------------------------------------------------------------------
 # decisions as a function of the query stream alone
 # ---------------------------------------------------------------------------

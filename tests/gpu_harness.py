@@ -58,9 +58,11 @@ def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] 
 
 def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 0,
             paged: Optional[bool] = None, q_override=None, poison: bool = False,
-            fused: bool = False) -> GpuRun:
-    """Prefill every sequence, then `steps` x (append, decode).  `record`
-    selects the steps whose outputs are copied back (default: all)."""
+            fused: bool = False, seed_q=None) -> GpuRun:
+    """Prefill every sequence, optionally seed the rings with the queries
+    `seed_q` [n, batch, Hq, d] of the last n prefill positions, then
+    `steps` x (append, decode).  `record` selects the steps whose outputs are
+    copied back (default: all)."""
     T = inp.q.shape[0] if steps is None else steps
     dev = torch.device("cuda")
     sess = make_session(w, inp, T, max_slices=max_slices, paged=paged)
@@ -72,6 +74,8 @@ def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 
     ctx = [int(c) for c in inp.contexts]
     for b in range(w.batch):
         sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
+    if seed_q is not None:
+        sess.seed(seed_q.to(dev).contiguous())
     q_all = (inp.q if q_override is None else q_override).to(dev)
     bidx = torch.arange(w.batch, device=dev)
     ctx_t = torch.tensor(ctx, device=dev)
@@ -109,7 +113,7 @@ class Report:
 
 def check_groups(w, inp, gpu: GpuRun, groups: Sequence[Tuple[int, int]],
                  steps: Optional[Sequence[int]] = None, K64=None, V64=None,
-                 tol: float = OUT_TOL) -> Report:
+                 tol: float = OUT_TOL, seed_q64=None) -> Report:
     """Replay the oracle for each KV group (b, g) over every step 0..T-1 and
     compare the recorded GPU steps.  `gpu` must hold every step for exact
     decision checks; steps missing from it are replayed without comparing."""
@@ -122,6 +126,8 @@ def check_groups(w, inp, gpu: GpuRun, groups: Sequence[Tuple[int, int]],
         Kg = (K64[b, g] if K64 is not None else inp.k[b, g].double().numpy())[None]
         Vg = (V64[b, g] if V64 is not None else inp.v[b, g].double().numpy())[None]
         heads = list(range(g * G, (g + 1) * G))
+        if seed_q64 is not None:
+            orc.seed(0, seed_q64[:, b, heads], Kg, Vg, int(inp.contexts[b]))
         for t in range(T):
             n = int(inp.contexts[b]) + t + 1
             p_new = max(0, n - w.band)

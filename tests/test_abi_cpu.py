@@ -105,6 +105,7 @@ def test_null_context_calls(B):
     assert lib.mac_prefill_kv(None, 16, 16, None, 0, 16, 16, 1, None) == 1
     assert lib.mac_read_kv(None, 16, 16, None, 0, 0, 1, 16, 16, None) == 1
     assert lib.mac_query_cache_push(None, 16, 16, 16, 16, 16, 16, None, None) == 1
+    assert lib.mac_seed_ring(None, 16, 1, 16, 16, None, None) == 1
     assert lib.mac_profile_enable(None, 1) == 1
     assert lib.mac_destroy(None) == 0
 

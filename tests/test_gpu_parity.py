@@ -184,3 +184,33 @@ def test_full_size_sampled_groups(name):
     say(f"[full:{name}] oracle replay of {groups}")
     rep = check_groups(w, inp, gpu, groups)
     assert_report(rep, f"full:{name}")
+
+
+# ---------------------------------------------------------------------------
+# ring seeding from the prefill
+# ---------------------------------------------------------------------------
+
+SEEDED = {
+    "8b_32k_seed_w": ("8b_32k", dict(context=2100, steps=24), 32),
+    "paged_seed_half": ("paged_b8", dict(ctx_range=(700, 1500), steps=16), 16),
+    "70b_seed": ("70b_128k", dict(batch=2, context=1200, steps=12), 64),
+    "tiny_seed_short_ctx": ("tiny", dict(context=10, steps=20, band=8, window=16), 10),
+}
+
+
+@pytest.mark.parametrize("name", list(SEEDED))
+def test_seeded_ring_every_step(name):
+    # the last n prefill positions are replayed into the rings; the decode
+    # queries continue the same stream, so the first decode step already hits
+    base, kw, n_hist = SEEDED[name]
+    w = workload(base, **kw)
+    full = make_inputs(w, steps=n_hist + w.steps)
+    hist, hist64 = full.q[:n_hist], full.q64[:n_hist]
+    inp = full.__class__(**{**full.__dict__, "q": full.q[n_hist:], "q64": full.q64[n_hist:]})
+    say(f"[seed:{name}] n_hist={n_hist} {w}")
+    gpu = run_gpu(w, inp, seed_q=hist)
+    rep = check_groups(w, inp, gpu, all_groups(w), seed_q64=hist64)
+    assert_report(rep, f"seed:{name}")
+    assert (gpu.match_n[0] >= 0).any(), "no hit on the first step after seeding"
+    lens = gpu.session.seq_lens.cpu().numpy()
+    np.testing.assert_array_equal(lens, inp.contexts + w.steps)

@@ -380,3 +380,56 @@ def test_hit_reads_golden():
         r = orc.step(0, q0, K[0], V[0], c["n"])
         assert r.hit.all() and (r.match_n == c["n_e"]).all()
         assert (r.keys_read == c["keys_read"]).all()
+
+
+# ---------------------------------------------------------------------------
+# ring seeding from a prefill
+# ---------------------------------------------------------------------------
+
+def test_seeded_entries_are_exact_prefix_states():
+    # each seeded entry is the scipy softmax attention of its own rotated
+    # query over [0, max(0, position + 1 - B)), with p and n of that position
+    w = small(band=8, window=6)
+    inp = make_inputs(w, steps=w.window)
+    N = int(inp.contexts[0])
+    K, V = inp.k.double().numpy(), inp.v.double().numpy()
+    orc = M.MacOracle.for_workload(w)
+    hist = inp.q64[:w.window, 0]
+    orc.seed(0, hist, K[0], V[0], N)
+    for h in range(w.n_q_heads):
+        ring = orc.rings[0][h]
+        assert len(ring) == w.window
+        for j, e in enumerate(ring):
+            pos = N - w.window + j
+            assert (e.p, e.n) == (max(0, pos + 1 - w.band), pos + 1)
+            g = h // w.group
+            qr = M.rope(hist[j, h], pos, w.rope_theta)
+            z = K[0, g, :e.p] @ qr / math.sqrt(w.head_dim)
+            np.testing.assert_allclose(e.o, softmax(z) @ V[0, g, :e.p], atol=1e-12)
+            assert abs(e.m + math.log(e.l) - logsumexp(z)) < 1e-10
+            np.testing.assert_array_equal(e.q, hist[j, h])
+
+
+def test_decode_after_seeding_matches_the_newest_seeded_query():
+    # the first decode query repeats the last prefill query: distance 0, the
+    # newest entry (context N) wins, and only the band and the tail are read
+    w = small(band=8, window=6)
+    inp = make_inputs(w, steps=w.window)
+    N = int(inp.contexts[0])
+    K, V = inp.k.double().numpy(), inp.v.double().numpy()
+    orc = M.MacOracle.for_workload(w)
+    orc.seed(0, inp.q64[:w.window, 0], K[0], V[0], N)
+    r = orc.step(0, inp.q64[w.window - 1, 0], K[0], V[0], N + 1)
+    assert r.hit.all()
+    assert (r.match_n == N).all()
+    assert (r.dist == 0).all()
+    assert (r.keys_read == (N + 1) - max(0, N - w.band)).all()
+
+
+def test_seeding_nothing_leaves_the_ring_empty():
+    w = small()
+    inp = make_inputs(w, steps=2)
+    orc = M.MacOracle.for_workload(w)
+    orc.seed(0, inp.q64[:0, 0], inp.k[0].double().numpy(), inp.v[0].double().numpy(),
+             int(inp.contexts[0]))
+    assert all(len(r) == 0 for r in orc.rings[0])
