@@ -16,7 +16,8 @@ path (every step misses: jump probability 1), i.e. algorithmic bytes / time;
 us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
 latency at contexts 8K..128K; `latency_classes` per-step p10/p50/p90 at
 jump probability 0.2 split by the step's decisions (every head hit, every
-head missed, mixed); `read_ceiling` the rate of a plain streaming-read
+head missed, mixed); `seeding` the cost of seeding the rings from the
+prefill (1 and W positions); `read_ceiling` the rate of a plain streaming-read
 kernel on the same device; `roofline` the step kernel's achieved bandwidth
 from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
 on a bounded sample of the same workload on the host cores.
@@ -251,6 +252,40 @@ def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache):
     return res
 
 
+def seeding_cost(w, cache):
+    """Time mac_seed_ring at the headline shape for the last prefill
+    position and for a full window (each position is one miss-path step),
+    and report whether the first decode step after it hits."""
+    import torch
+    from synth.streams import make_q_stream
+    res = []
+    for n_hist in (1, w.window):
+        Ls = make_layers(w, 0.0, 4, 1, cache)
+        L = Ls[0]
+        q, _ = make_q_stream(w, p_jump=0.0, layer=7, steps=n_hist + 1)
+        dev = torch.device("cuda")
+        hist = q[:n_hist].to(dev).contiguous()
+        L.q = q[n_hist:].to(dev).contiguous()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.sess.seed(hist)
+        e1.record(stream)
+        L.step()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        first_hit = float((L.match_n[0] >= 0).float().mean().item())
+        res.append({"n_hist": n_hist, "ms": ms, "us_per_position": 1e3 * ms / n_hist,
+                    "first_step_hit_rate": first_hit})
+        log(f"  seed {n_hist} positions: {ms:.3f} ms, first decode step hit rate {first_hit:.2f}")
+        L.sess.close()
+        del Ls, L
+        torch.cuda.empty_cache()
+    return res
+
+
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
@@ -378,6 +413,7 @@ def main():
     ap.add_argument("--no-flatness", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-seed", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--points", type=str, default="")
@@ -469,6 +505,12 @@ def main():
             log(f"  {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / {v['p50_us']:.1f} / "
                 f"{v['p90_us']:.1f} us")
 
+    # ---- ring seeding from the prefill
+    seed = None
+    if not args.no_seed:
+        log("ring seeding at 131072 keys")
+        seed = seeding_cost(w, cache)
+
     # ---- streaming-read ceiling of this device, same run
     ceil = None
     if not args.no_ceiling:
@@ -508,6 +550,7 @@ def main():
         "sweep": sweep,
         "flatness": flat_steps,
         "latency_classes": lat,
+        "seeding": seed,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,
