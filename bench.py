@@ -17,7 +17,9 @@ us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
 latency at contexts 8K..128K; `latency_classes` per-step p10/p50/p90 at
 jump probability 0.2 split by the step's decisions (every head hit, every
 head missed, mixed); `seeding` the cost of seeding the rings from the
-prefill (1 and W positions); `read_ceiling` the rate of a plain streaming-read
+prefill (1 and W positions); `drift` the largest |out_MAC - out_dense| on a
+16K continuous-generation stream by reuse-chain depth, over tau and B;
+`read_ceiling` the rate of a plain streaming-read
 kernel on the same device; `roofline` the step kernel's achieved bandwidth
 from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
 on a bounded sample of the same workload on the host cores.
@@ -286,6 +288,100 @@ def seeding_cost(w, cache):
     return res
 
 
+def chain_depths(match_n, contexts):
+    """Reuse-chain depth of the entry each (step, sequence, head) pushes: 0
+    after a miss, else one more than the depth of the entry it reused (found
+    by its context length).  match_n: [T, batch, Hq]; rings start empty."""
+    T, nb, hq = match_n.shape
+    depth = np.zeros((T, nb, hq), np.int64)
+    for b in range(nb):
+        for h in range(hq):
+            by_n = {}
+            for t in range(T):
+                m = int(match_n[t, b, h])
+                d = by_n[m] + 1 if m >= 0 else 0
+                depth[t, b, h] = d
+                by_n[int(contexts[b]) + t + 1] = d
+    return depth
+
+
+def drift_run(w, steps, inputs=None):
+    """Run one query stream through two sessions on the same KV: the MAC
+    configuration of `w`, and W = 0, which never matches and so computes
+    plain attention over every key.  Returns per (step, sequence, head) the
+    largest |out_MAC - out_dense| over the head dimension, the MAC side's
+    matched context lengths, and the inputs."""
+    import torch
+    from kv_cache_reuse_amd import binding as B
+    from synth.streams import make_inputs
+    inp = make_inputs(w, steps=steps) if inputs is None else inputs
+    dev = torch.device("cuda")
+    mc = int(inp.contexts.max()) + steps
+    sess = [B.MacSession(B.config_from_workload(x, max_context=mc))
+            for x in (w, w.replace(window=0))]
+    K, V = inp.k.to(dev), inp.v.to(dev)
+    for s_ in sess:
+        for b in range(w.batch):
+            n0 = int(inp.contexts[b])
+            s_.prefill(b, K[b, :, :n0], V[b, :, :n0])
+    q = inp.q.to(dev)
+    bidx = torch.arange(w.batch, device=dev)
+    ctx_t = torch.tensor([int(c) for c in inp.contexts], device=dev)
+    dmax = torch.empty((steps, w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    match_n = torch.empty((steps, w.batch, w.n_q_heads), dtype=torch.int32, device=dev)
+    for t in range(steps):
+        pos = ctx_t + t
+        k_new = K[bidx, :, pos].contiguous()
+        v_new = V[bidx, :, pos].contiguous()
+        o_mac, m_mac, _ = sess[0].decode_append(q[t], k_new, v_new)
+        o_den, _, _ = sess[1].decode_append(q[t], k_new, v_new, match_ctx=False, dist=False)
+        dmax[t] = (o_mac - o_den).abs().amax(dim=-1)
+        match_n[t] = m_mac
+    torch.cuda.synchronize()
+    res = dmax.cpu().numpy(), match_n.cpu().numpy(), inp
+    for s_ in sess:
+        s_.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+DEPTH_BUCKETS = ((0, 0), (1, 1), (2, 3), (4, 7), (8, 15), (16, 31), (32, 1 << 30))
+
+
+def drift_summary(dmax, match_n, contexts):
+    depth = chain_depths(match_n, contexts)
+    rows = []
+    for lo, hi in DEPTH_BUCKETS:
+        sel = (depth >= lo) & (depth <= hi)
+        if sel.any():
+            rows.append({"depth": [lo, hi if hi < (1 << 30) else None], "count": int(sel.sum()),
+                         "max": float(dmax[sel].max()), "mean": float(dmax[sel].mean())})
+    return {"hit_rate": float((match_n >= 0).mean()), "max_drift": float(dmax.max()),
+            "max_depth": int(depth.max()), "by_depth": rows}
+
+
+def drift_sweep(steps):
+    """Drift of MAC from dense attention along chains of hits on a 16K
+    continuous-generation stream, for tau in {0.30, 0.32, 0.35, 0.5} sqrt(d)
+    (consecutive queries of the stream lie about 0.32 sqrt(d) apart) and B in
+    {64, 256, 1024}."""
+    from synth.streams import workload
+    base = workload("gen_16k")
+    out = []
+    for f in (0.30, 0.32, 0.35, 0.5):
+        for band in (64, 256, 1024):
+            w = base.replace(tau=f * math.sqrt(base.head_dim), band=band)
+            dmax, mn, inp = drift_run(w, steps)
+            s = drift_summary(dmax, mn, inp.contexts)
+            s.update({"tau_over_sqrt_d": f, "band": band})
+            out.append(s)
+            deep = s["by_depth"][-1]
+            log(f"  tau {f:.2f} sqrt(d), B {band}: hit {s['hit_rate']:.3f}, max drift "
+                f"{s['max_drift']:.2e}, deepest chain {s['max_depth']} "
+                f"(depth {deep['depth'][0]}+: max {deep['max']:.2e})")
+    return out
+
+
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
@@ -414,6 +510,8 @@ def main():
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-seed", action="store_true")
+    ap.add_argument("--no-drift", action="store_true")
+    ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--points", type=str, default="")
@@ -511,6 +609,12 @@ def main():
         log("ring seeding at 131072 keys")
         seed = seeding_cost(w, cache)
 
+    # ---- drift from dense attention along chains of hits (16K generation)
+    drift = None
+    if not args.no_drift:
+        log(f"drift: gen_16k, {args.drift_steps} steps per point")
+        drift = drift_sweep(args.drift_steps)
+
     # ---- streaming-read ceiling of this device, same run
     ceil = None
     if not args.no_ceiling:
@@ -551,6 +655,7 @@ def main():
         "flatness": flat_steps,
         "latency_classes": lat,
         "seeding": seed,
+        "drift": drift,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -10,6 +10,7 @@ generation) are stood in for by the five synthetic shapes below:
 * ``8b_128k``  - the same shape at 131072 keys (the headline shape)
 * ``paged_b8`` - 8 sequences with contexts uniform in [16384, 65536], 16-key pages
 * ``70b_128k`` - 4 sequences, 64 query / 8 KV heads, 131072 keys, 1% outlier keys x8
+* ``gen_16k``  - 1 sequence, 8B shape, 16384-key prefill, 2048 generated tokens
 
 Query stream (pre-RoPE), per sequence b: ``q_0 ~ N(0, I)``; for t >= 1 a single
 Bernoulli(p) per (b, t) decides a jump, which redraws the whole token's query
@@ -116,6 +117,13 @@ WORKLOADS = {
         rope_theta=5e5, rho=0.9, p_jump=0.1, window=64, band=256,
         tau=_TAU_HALF_SQRT_D128, rho_range=(0.8, 0.99), outlier_p=0.01,
         outlier_scale=8.0),
+    # long continuous generation from a 16K prefill (the shape of the
+    # pages' 16K continuous-generation suite), for the drift of the reused
+    # states along chains of hits
+    "gen_16k": Workload(
+        name="gen_16k", index=6, batch=1, n_q_heads=32, n_kv_heads=8,
+        head_dim=128, dtype="bf16", context=16384, steps=2048, rope_theta=5e5,
+        rho=0.95, p_jump=0.05, window=32, band=256, tau=_TAU_HALF_SQRT_D128),
 }
 
 # jump probabilities of the headline hit-rate sweep (about 0/50/80/95% hits)

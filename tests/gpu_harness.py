@@ -113,10 +113,12 @@ class Report:
 
 def check_groups(w, inp, gpu: GpuRun, groups: Sequence[Tuple[int, int]],
                  steps: Optional[Sequence[int]] = None, K64=None, V64=None,
-                 tol: float = OUT_TOL, seed_q64=None) -> Report:
+                 tol: float = OUT_TOL, seed_q64=None, collect=None) -> Report:
     """Replay the oracle for each KV group (b, g) over every step 0..T-1 and
     compare the recorded GPU steps.  `gpu` must hold every step for exact
-    decision checks; steps missing from it are replayed without comparing."""
+    decision checks; steps missing from it are replayed without comparing.
+    With `collect` (a dict), the oracle's outputs and decisions are stored in
+    it under (b, g, t)."""
     T = max(gpu.out) + 1 if steps is None else max(steps) + 1
     G = w.group
     rep = Report()
@@ -164,6 +166,8 @@ def check_groups(w, inp, gpu: GpuRun, groups: Sequence[Tuple[int, int]],
                     else:
                         rep.mismatches.append((b, h, t, "decision", g_n, o_n, mt.dist, gd))
             r = orc.step(0, q, Kg, Vg, n, force=force or None)
+            if collect is not None:
+                collect[(b, g, t)] = (r.out.copy(), r.match_n.copy())
             if have:
                 err = np.abs(gpu.out[t][b, heads].astype(np.float64) - r.out)
                 e = float(np.nanmax(err)) if err.size else 0.0

@@ -433,3 +433,29 @@ def test_seeding_nothing_leaves_the_ring_empty():
     orc.seed(0, inp.q64[:0, 0], inp.k[0].double().numpy(), inp.v[0].double().numpy(),
              int(inp.contexts[0]))
     assert all(len(r) == 0 for r in orc.rings[0])
+
+
+def test_reuse_chain_depths():
+    # 0 after a miss, else one more than the reused entry's depth
+    import bench
+    mn = np.array([-1, 1001, 1002, -1, 1004, 1002]).reshape(-1, 1, 1)
+    d = bench.chain_depths(mn, np.array([1000]))[:, 0, 0]
+    assert d.tolist() == [0, 1, 2, 0, 1, 2]   # the entry of context 1002 has depth 1
+
+
+def test_a_miss_is_dense_attention_in_the_oracle():
+    # the drift of MAC from dense attention is zero (to rounding) on misses
+    w = small(p_jump=0.3)
+    inp = make_inputs(w)
+    res, _ = M.run(w, inp)
+    K, V = inp.k.double().numpy(), inp.v.double().numpy()
+    misses = 0
+    for t, row in enumerate(res):
+        r = row[0]
+        qr = M.rope(inp.q64[t, 0], r.n - 1, w.rope_theta)
+        for h in np.nonzero(~r.hit)[0]:
+            g = h // w.group
+            np.testing.assert_allclose(r.out[h], M.dense(qr[h:h + 1], K[0, g, :r.n],
+                                                         V[0, g, :r.n])[0], atol=1e-12)
+            misses += 1
+    assert misses > 5
