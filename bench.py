@@ -19,6 +19,7 @@ jump probability 0.2 split by the step's decisions (every head hit, every
 head missed, mixed); `seeding` the cost of seeding the rings from the
 prefill (1 and W positions); `drift` the largest |out_MAC - out_dense| on a
 16K continuous-generation stream by reuse-chain depth, over tau and B;
+`multilayer` every layer of a token in one graph (32 layers, 16K keys);
 `read_ceiling` the rate of a plain streaming-read
 kernel on the same device; `roofline` the step kernel's achieved bandwidth
 from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
@@ -382,6 +383,27 @@ def drift_sweep(steps):
     return out
 
 
+def multilayer(layers=32, tokens=32):
+    """Every layer of a token in one HIP graph: `layers` layer copies of the
+    16K-context 8B shape (own caches and rings), visited in order for each
+    token, `tokens` tokens captured in one graph and replayed once.  Reports
+    the time per token across all layers and per layer step."""
+    from synth.streams import workload
+    w = workload("gen_16k")
+    out = []
+    cache = {}
+    for p in (0.05, 1.0):
+        steps = layers * tokens
+        ms, recs, _, _ = run_point(w, p, steps, layers * 2, layers, inputs_cache=cache)
+        st = summarize(w, ms, recs, steps)
+        out.append({"p_jump": p, "layers": layers, "tokens": tokens,
+                    "us_per_token_all_layers": 1e3 * ms / tokens,
+                    "us_per_layer_step": 1e3 * ms / steps, "hit_rate": st["hit_rate"]})
+        log(f"  {layers} layers, p={p}: {1e3 * ms / tokens:.0f} us per token "
+            f"({1e3 * ms / steps:.2f} us per layer step, hit {st['hit_rate']:.3f})")
+    return out
+
+
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
@@ -511,6 +533,7 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-seed", action="store_true")
     ap.add_argument("--no-drift", action="store_true")
+    ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -615,6 +638,12 @@ def main():
         log(f"drift: gen_16k, {args.drift_steps} steps per point")
         drift = drift_sweep(args.drift_steps)
 
+    # ---- every layer of a token in one graph (16K context, 32 layers)
+    multi = None
+    if not args.no_multilayer:
+        log("multi-layer graph: gen_16k shape, 32 layers")
+        multi = multilayer()
+
     # ---- streaming-read ceiling of this device, same run
     ceil = None
     if not args.no_ceiling:
@@ -656,6 +685,7 @@ def main():
         "latency_classes": lat,
         "seeding": seed,
         "drift": drift,
+        "multilayer": multi,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,
