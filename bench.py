@@ -20,6 +20,7 @@ head missed, mixed); `seeding` the cost of seeding the rings from the
 prefill (1 and W positions); `drift` the largest |out_MAC - out_dense| on a
 16K continuous-generation stream by reuse-chain depth, over tau and B;
 `multilayer` every layer of a token in one graph (32 layers, 16K keys);
+`mqa` 32 query heads over one KV head at 128K keys;
 `read_ceiling` the rate of a plain streaming-read
 kernel on the same device; `roofline` the step kernel's achieved bandwidth
 from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
@@ -404,6 +405,27 @@ def multilayer(layers=32, tokens=32):
     return out
 
 
+def mqa(steps, warmup, cache=None):
+    """MQA at the headline context: 32 query heads over one KV head (the
+    32-head group runs as two 16-head chunks over the same KV).  Miss path
+    with the step kernel timed by HIP events, and the all-hit step."""
+    from synth.streams import workload
+    w = workload("8b_128k", n_kv_heads=1)
+    ms, recs, kms, kl = run_point(w, 1.0, steps, warmup, 2, kernel_timing=True,
+                                  inputs_cache=cache)
+    st = summarize(w, ms, recs, steps)
+    kbytes = 131073 * 2 * w.head_dim * w.bytes_per_elem
+    msh, rh, _, _ = run_point(w, 0.0, steps, warmup, 2, inputs_cache=cache)
+    sh = summarize(w, msh, rh, steps)
+    res = {"workload": "8b_128k with 1 KV head: 32 query heads in 2 chunks of 16",
+           "miss_us_per_step": st["us_per_step"], "miss_kernel_us": 1e3 * kms / max(kl, 1),
+           "miss_kernel_GBps": kbytes / (kms / 1e3 / max(kl, 1)) / 1e9,
+           "hit_us_per_step": sh["us_per_step"], "hit_rate": sh["hit_rate"]}
+    log(f"  MQA miss: {res['miss_us_per_step']:.1f} us/step (kernel {res['miss_kernel_us']:.1f} us, "
+        f"{res['miss_kernel_GBps']:.0f} GB/s of KV); all-hit {res['hit_us_per_step']:.2f} us/step")
+    return res
+
+
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
@@ -534,6 +556,7 @@ def main():
     ap.add_argument("--no-seed", action="store_true")
     ap.add_argument("--no-drift", action="store_true")
     ap.add_argument("--no-multilayer", action="store_true")
+    ap.add_argument("--no-mqa", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -644,6 +667,12 @@ def main():
         log("multi-layer graph: gen_16k shape, 32 layers")
         multi = multilayer()
 
+    # ---- MQA / groups wider than the 16-head tile
+    mq = None
+    if not args.no_mqa:
+        log("MQA: 32 query heads over 1 KV head at 131072 keys")
+        mq = mqa(min(args.steps, 128), args.warmup)
+
     # ---- streaming-read ceiling of this device, same run
     ceil = None
     if not args.no_ceiling:
@@ -686,6 +715,7 @@ def main():
         "seeding": seed,
         "drift": drift,
         "multilayer": multi,
+        "mqa": mq,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,

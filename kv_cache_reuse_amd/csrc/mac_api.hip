@@ -54,6 +54,14 @@ struct Layout {
 
 int elem_size(int dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
 
+// A KV head with G > kMaxGroup query heads is processed as nchunk groups of
+// G / nchunk heads (the matrix-core tile is 16 heads wide).
+int n_chunks(const mac_config* c) {
+  const int G = c->n_q_heads / c->n_kv_heads;
+  return (G + mac::kMaxGroup - 1) / mac::kMaxGroup;
+}
+int chunk_heads(const mac_config* c) { return c->n_q_heads / c->n_kv_heads / n_chunks(c); }
+
 mac_status check_config(const mac_config* c) {
   if (!c) return fail(MAC_ERR_INVALID_ARG, "config is NULL");
   if (c->batch < 1) return fail(MAC_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", c->batch);
@@ -63,9 +71,13 @@ mac_status check_config(const mac_config* c) {
   if (c->n_q_heads % c->n_kv_heads)
     return fail(MAC_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
                 c->n_q_heads, c->n_kv_heads);
-  if (c->n_q_heads / c->n_kv_heads > mac::kMaxGroup)
-    return fail(MAC_ERR_UNSUPPORTED, "query heads per KV head must be <= %d (got %d)", mac::kMaxGroup,
-                c->n_q_heads / c->n_kv_heads);
+  {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    const int nc = (G + mac::kMaxGroup - 1) / mac::kMaxGroup;
+    if (G % nc)
+      return fail(MAC_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d must split into "
+                  "%d equal groups of at most %d", G, mac::kMaxGroup, nc, mac::kMaxGroup);
+  }
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(MAC_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
   if (c->dtype != MAC_DTYPE_F32 && c->dtype != MAC_DTYPE_BF16)
@@ -108,7 +120,7 @@ Layout layout(const mac_config* c) {
 
   L.capacity = c->page_size ? (int64_t)c->max_pages_per_seq * mac::kTile : (int64_t)c->max_context;
   L.tiles_per_seq = c->page_size ? 0 : mac::ceil_div(c->max_context, mac::kTile);
-  const int groups = c->batch * c->n_kv_heads;
+  const int groups = c->batch * c->n_kv_heads * n_chunks(c);   // matched groups
   int S = c->max_slices;
   if (S == 0) {
     // never more slices than the longest context can fill
@@ -118,7 +130,7 @@ Layout layout(const mac_config* c) {
     if (S > mac::kMaxSlices) S = mac::kMaxSlices;
     if (S < 2) S = 2;
   }
-  const size_t G = c->n_q_heads / c->n_kv_heads;
+  const size_t G = chunk_heads(c);
   if (S * G > (size_t)mac::kMergeCap) S = mac::kMergeCap / (int)G;
   L.slices = S;
   off = 0;
@@ -351,8 +363,9 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.geom = ctx->geom();
   a.batch = c.batch;
   a.hq = c.n_q_heads;
-  a.hkv = c.n_kv_heads;
-  a.group = c.n_q_heads / c.n_kv_heads;
+  a.nchunk = n_chunks(&c);
+  a.hkv = c.n_kv_heads * a.nchunk;
+  a.group = chunk_heads(&c);
   a.band = c.band;
   a.tau2 = static_cast<float>((double)c.tau * (double)c.tau);
   a.theta = c.rope_theta;

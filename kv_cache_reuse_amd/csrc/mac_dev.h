@@ -229,7 +229,10 @@ struct StepArgs {
   PartialView part;
   RingView ring;
   KvGeom geom;
-  int batch, hq, hkv, group, band;
+  // A KV head with more than kMaxGroup query heads is split into nchunk
+  // groups of `group` heads each ("virtual" KV heads; hkv counts them); KV
+  // addressing uses the real head, virtual index / nchunk.
+  int batch, hq, hkv, group, band, nchunk;
   float tau2;               // tau^2 rounded to fp32
   double theta;
 };

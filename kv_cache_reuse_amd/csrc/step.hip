@@ -309,6 +309,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int grp = blockIdx.x % n_groups;
   const int slice = blockIdx.x / n_groups;
   const int b = grp / a.hkv, kvh = grp % a.hkv;
+  const int kvr = kvh / a.nchunk;          // the KV head whose cache is read
   const int G = a.group;
   // the wave index is the same in every lane of a wave; readfirstlane makes
   // that visible to the compiler, so per-wave loop bounds and branches are
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   KvGeom geom = a.geom;
   geom.paged = PAGED ? 1 : 0;
   auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
-    const int64_t base = tile_base(geom, a.page_table, b, kvh, tt);
+    const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
     const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
     const u4* vp = reinterpret_cast<const u4*>(vc + base) + lane;
 #pragma unroll
@@ -367,8 +368,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const bool early_patch = append && ps.n_post > 0 && slice == ps.n_post - 1;
   T pke = T(0), pve = T(0);
   if (early_patch && tid < D) {
-    pke = static_cast<const T*>(a.k_new)[((size_t)b * a.hkv + kvh) * D + tid];
-    pve = static_cast<const T*>(a.v_new)[((size_t)b * a.hkv + kvh) * D + tid];
+    pke = static_cast<const T*>(a.k_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
+    pve = static_cast<const T*>(a.v_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
   }
   match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi, wave < G);
   for (int hi = wave + 4; hi < G; hi += 4) {
@@ -432,8 +433,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     // would stay live through the whole tile loop); with slices after p_new
     // that happened during the match, else (B = 0) it happens here
     if (patcher && !early_patch) {
-      const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.hkv + kvh) * D;
-      const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.hkv + kvh) * D;
+      const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.geom.hkv + kvr) * D;
+      const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.geom.hkv + kvr) * D;
       for (int e = tid; e < D; e += 256) {
         pk[e] = kn[e];
         pv[e] = vn[e];
@@ -633,8 +634,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     // The new token goes into the cache only now: stores count in the same
     // counter as loads, and one issued before the tile loop would be waited
     // for at its entry.  No other workgroup reads this slot in this step.
-    if (patcher && wave == 0) {
-      const int64_t base = tile_base_w(geom, a.page_table, b, kvh, tnew);
+    // (with a split KV head, every chunk patches its own tile and the first
+    // one writes the cache)
+    if (patcher && wave == 0 && kvh % a.nchunk == 0) {
+      const int64_t base = tile_base_w(geom, a.page_table, b, kvr, tnew);
       if (base >= 0) {
         T* kw = const_cast<T*>(kc);
         T* vw = const_cast<T*>(vc);

@@ -49,6 +49,11 @@ SMALL = {
     "d64_bf16": ("8b_32k", dict(head_dim=64, context=1500, steps=24, tau=0.5 * math.sqrt(64))),
     "d128_f32": ("tiny", dict(head_dim=128, n_q_heads=8, n_kv_heads=2, context=900, steps=24,
                               tau=0.5 * math.sqrt(128))),
+    # groups wider than the 16-head matrix tile: split into equal chunks
+    "mqa_g32": ("8b_32k", dict(n_kv_heads=1, context=2500, steps=24)),
+    "mqa_g64": ("8b_32k", dict(n_q_heads=64, n_kv_heads=1, context=1800, steps=16)),
+    "g20": ("8b_32k", dict(n_q_heads=40, n_kv_heads=2, context=1200, steps=16)),
+    "mqa_paged": ("paged_b8", dict(batch=2, n_kv_heads=1, ctx_range=(500, 1200), steps=12)),
 }
 
 
@@ -78,7 +83,7 @@ def test_stale_cache_slots_do_not_leak(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_full", "8b_128k_p05", "paged_b8_small", "70b_small",
-                                  "ctx1"])
+                                  "ctx1", "mqa_g32", "mqa_paged"])
 def test_fused_append_decode_every_step(name):
     base, kw = SMALL[name]
     w = workload(base, **kw)
@@ -169,13 +174,14 @@ FULL = {
     "8b_128k_p02": (dict(p_jump=0.2), 96, [(0, 3)]),
     "paged_b8": (dict(), 64, [(2, 1), (7, 6)]),
     "70b_128k": (dict(), 40, [(1, 2)]),
+    "8b_128k_mqa": (dict(n_kv_heads=1, p_jump=0.2), 24, [(0, 0)]),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled_groups(name):
     kw, steps, groups = FULL[name]
-    base = name.split("_p0")[0]
+    base = name.split("_p0")[0].replace("_mqa", "")
     w = workload(base, **kw)
     say(f"[full:{name}] generating")
     inp = make_inputs(w, steps=steps)
