@@ -34,6 +34,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mac_dev.h"
 #include "mac_launch.h"
 
@@ -296,7 +298,10 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
 }
 
 // ========================================================== the kernel ==
-template <typename T, int D, bool PAGED>
+// WIDE: groups of more than 4 query heads (each wave matches several); a
+// separate instantiation so that the narrow case's code has no conditional
+// loads (which make the compiler wait for every load in flight).
+template <typename T, int D, bool PAGED, bool WIDE>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int E = 16 / (int)sizeof(T);
@@ -338,8 +343,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   // (waves past the group's heads load a valid head's rows and ignore them:
   // no branch, so the compiler need not wait for the loads at a join)
   const int bh0 = b * a.hq + kvh * G + (wave < G ? wave : 0);
-  MatchIn<T, D> mi;
-  match_load<T, D>(a, bh0, lane, mi);
+  // groups wider than the 4 waves: a second buffer takes the wave's next
+  // head right behind the first, and later heads are loaded one match ahead
+  MatchIn<T, D> mi[WIDE ? 2 : 1];
+  match_load<T, D>(a, bh0, lane, mi[0]);
+  if constexpr (WIDE) match_load<T, D>(a, wave + 4 < G ? bh0 + 4 : bh0, lane, mi[1]);
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
@@ -371,10 +379,21 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     pke = static_cast<const T*>(a.k_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
     pve = static_cast<const T*>(a.v_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
   }
-  match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi, wave < G);
-  for (int hi = wave + 4; hi < G; hi += 4) {
-    match_load<T, D>(a, bh0 + (hi - wave), lane, mi);
-    match_compute<T, D>(a, sh, bh0 + (hi - wave), hi, lane, n, p_new, mi);
+  match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi[0], wave < G);
+  if constexpr (WIDE) {
+    // heads 4 r + wave, r = 1 .. 3, with the buffers chosen at compile time
+    auto more = [&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const int hi = wave + 4 * r;
+      if (hi < G) {
+        if (hi + 4 < G) match_load<T, D>(a, bh0 + 4 * (r + 1), lane, mi[(r + 1) & 1]);
+        match_compute<T, D>(a, sh, bh0 + 4 * r, hi, lane, n, p_new, mi[r & 1]);
+      }
+    };
+    static_assert(kMaxGroup == 16, "four heads per wave at most");
+    more(std::integral_constant<int, 1>{});
+    more(std::integral_constant<int, 2>{});
+    more(std::integral_constant<int, 3>{});
   }
   if (early_patch && tid < D) {
     pk[tid] = pke;
@@ -887,9 +906,12 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
                        hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0) (void)hipEventRecord(ev0, st);
   const int grid = a.batch * a.hkv * a.part.S;
-#define L_STEP(T, D)                                                                           \
-  if (paged) hipLaunchKernelGGL((step_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, a);  \
-  else hipLaunchKernelGGL((step_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, a)
+  const bool wide = a.group > 4;
+#define L_STEP(T, D)                                                                              \
+  if (paged && wide) hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, a); \
+  else if (paged) hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(256), 0, st, a);  \
+  else if (wide) hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(256), 0, st, a);   \
+  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(256), 0, st, a)
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
   if (ev1) (void)hipEventRecord(ev1, st);
