@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   MAC_OK = 0,
   MAC_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or value   */
-  MAC_ERR_UNSUPPORTED = 2,  /* valid but not built (head_dim, dtype, G>16)  */
+  MAC_ERR_UNSUPPORTED = 2,  /* valid but not built (head_dim, dtype, G)     */
   MAC_ERR_CAPACITY = 3,     /* a sequence would exceed its KV capacity      */
   MAC_ERR_DEVICE = 4,       /* a HIP call failed; the message has its code  */
   MAC_ERR_STATE = 5         /* context poisoned by an earlier device error  */
@@ -79,7 +79,8 @@ typedef enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 } mac_dtype;
 typedef struct {
   int32_t batch;             /* sequences, >= 1                              */
   int32_t n_q_heads;         /* Hq, a multiple of n_kv_heads                 */
-  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv must be <= 16              */
+  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv <= 16, or G splitting into */
+                             /* ceil(G/16) equal groups (MQA: 32, 64, ...)   */
   int32_t head_dim;          /* d: 64 or 128                                 */
   int32_t dtype;             /* mac_dtype of q, keys, values and ring q      */
   int32_t max_context;       /* contiguous cache: keys per sequence          */
@@ -183,6 +184,10 @@ mac_status mac_decode_step(mac_ctx* ctx, const void* q_pre,
  * position attends to keys [0, seq_lens_dev[b] + 1), and seq_lens_dev[b]
  * is incremented.  Results are bitwise identical to the two calls.  Returns
  * MAC_ERR_CAPACITY if any sequence is full (host mirror).
+ * Graph capture: the kernels read the lengths and ring counts on the
+ * device, so each replay of a captured call performs the next step (a
+ * full sequence's append is dropped on the device); the host mirror, and
+ * with it the capacity check, advances once, at capture.
  */
 mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k_new,
                                   const void* v_new, void* k_cache, void* v_cache,

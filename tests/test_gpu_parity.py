@@ -220,3 +220,54 @@ def test_seeded_ring_every_step(name):
     assert (gpu.match_n[0] >= 0).any(), "no hit on the first step after seeding"
     lens = gpu.session.seq_lens.cpu().numpy()
     np.testing.assert_array_equal(lens, inp.contexts + w.steps)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["8b_32k_ragged", "paged_b8_small"])
+def test_graph_replays_equal_eager_steps(name):
+    # one fused decode step is captured once and replayed for every token,
+    # its input buffers refilled by eager copies between replays; every
+    # replay must equal the eagerly launched step bitwise (the kernels read
+    # the lengths and ring counts on the device, so each replay advances)
+    from kv_cache_reuse_amd import binding as B
+    from tests.gpu_harness import make_session
+    base, kw = SMALL[name]
+    w = workload(base, **{**kw, "steps": 12})
+    inp = make_inputs(w)
+    ref = run_gpu(w, inp, fused=True)
+    T = w.steps
+    dev = torch.device("cuda")
+    sess = make_session(w, inp, T)
+    K, V = inp.k.to(dev), inp.v.to(dev)
+    ctx = [int(c) for c in inp.contexts]
+    for b in range(w.batch):
+        sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
+    bidx = torch.arange(w.batch, device=dev)
+    ctx_t = torch.tensor(ctx, device=dev)
+    q_all = inp.q.to(dev)
+    q_buf = torch.empty_like(q_all[0])
+    k_buf = torch.empty((w.batch, w.n_kv_heads, w.head_dim), dtype=q_all.dtype, device=dev)
+    v_buf = torch.empty_like(k_buf)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.mac_decode_step_append(sess.ctx, q_buf.data_ptr(), k_buf.data_ptr(), v_buf.data_ptr(),
+                                 sess.k_cache.data_ptr(), sess.v_cache.data_ptr(), sess._pt(),
+                                 sess.out.data_ptr(), sess.match_ctx.data_ptr(),
+                                 sess.dist.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for t in range(T):
+        pos = ctx_t + t
+        q_buf.copy_(q_all[t])
+        k_buf.copy_(K[bidx, :, pos])
+        v_buf.copy_(V[bidx, :, pos])
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sess.out.cpu().numpy(), ref.out[t])
+        np.testing.assert_array_equal(sess.match_ctx.cpu().numpy(), ref.match_n[t])
+        np.testing.assert_array_equal(sess.dist.cpu().numpy(), ref.dist[t])
+    np.testing.assert_array_equal(sess.seq_lens.cpu().numpy(), inp.contexts + T)
+    del g
