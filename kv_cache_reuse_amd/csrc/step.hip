@@ -699,6 +699,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
   }
 
+
   // the match results, for the merge kernel and the optional outputs (last,
   // for the same reason as the token's store)
   if (slice == 0 && tid < G) {
@@ -710,155 +711,108 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 }
 
 // ========================================================= merge kernel ==
-// One 256-thread workgroup per query head (b, h): log-sum-exp merge of the
+// Merge of one query head (b, h) by one wave: log-sum-exp merge of the
 // reused state and the group's slices, the head's new ring entry and its
-// output.  Two rounds of loads: the group's match results together with
-// every slice's (m, l) and this thread's first slice outputs (slices the
-// plan does not use hold stale values: they are read in bounds and never
-// enter the arithmetic), then the reused ring state, whose latency hides
-// behind the slice reductions: it joins as one last two-way merge.  Thread
-// (sub, quad) folds every NSUB-th slice's 4 consecutive output dims with
-// 16-byte loads.  All reductions run in a fixed order, so results are
-// bitwise reproducible.
+// output.  No barrier: lane k takes the (m, l) of slices k, k + 64, ... (kept
+// in LDS for the wave, `sm`/`sl`), each lane owns D/64 output dims and folds
+// the slices' o in slice order with the weights read back from LDS, so
+// results are bitwise reproducible.  One round of loads brings every
+// slice's (m, l), the first kBatch slices' o and the query the entry copies
+// (slices the plan leaves unused hold stale values: read in bounds, never
+// used); the reused ring state follows in a second round that overlaps the
+// reductions and joins last as a two-way merge.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
-  constexpr int NQ4 = D / 4;            // float4 quads of one head's output
-  constexpr int NSUB = 256 / NQ4;       // slice subsets folded in parallel
-  constexpr int kBatch = 8;             // loads in flight per thread per round
-  constexpr int kMl = kMaxSlices / 256; // (m, l) loads per thread
-  const int bh = blockIdx.x;
+__device__ __forceinline__ void merge_head(const StepArgs& a, const Plan& p, int n,
+                                           const HeadState& hs, int bh, int grp, int hi,
+                                           int lane, float* sm, float* sl) {
+  constexpr int DL = D / 64;            // output dims per lane
+  constexpr int kBatch = 32;            // slices whose o is loaded per round
   const int b = bh / a.hq, h = bh % a.hq;
-  const int G = a.group, kvh = h / G, hi = h % G;
-  const int S = a.part.S, grp = b * a.hkv + kvh;
-  // the wave index is the same in every lane of a wave; readfirstlane makes
-  // that visible to the compiler, so per-wave loop bounds and branches are
-  // scalar (vector control flow around loads makes it wait for all of them)
-  const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int sub = tid / NQ4, d4 = tid % NQ4;
+  const int G = a.group, S = a.part.S;
   const RingView& R = a.ring;
-  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
-  const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
   const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
-
-  __shared__ float sw[kMaxSlices];
-  __shared__ float sl[kMaxSlices];
-  __shared__ float red[4][4];
-  __shared__ float4 rp[NSUB][NQ4];
-  __shared__ float4 rq[NSUB][NQ4];
-
-  // ---- round 1 (with the query the new ring entry copies)
-  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + 4 * d4;
-  T qv[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qv[e] = qsrc[e];
-  const HeadState hs = hsg[hi];
-  int lo = hsg[0].s;
-  for (int i = 1; i < G; ++i) lo = min(lo, hsg[i].s);
-  float2 mlk[kMl];
-#pragma unroll
-  for (int u = 0; u < kMl; ++u) {
-    const int k = tid + 256 * u;
-    if (k < S) mlk[u] = pml[pbase + (size_t)k * G];
-  }
-  float4 v0[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int k = min(sub + u * NSUB, S - 1);
-    v0[u] = reinterpret_cast<const float4*>(a.part.o + (pbase + (size_t)k * G) * D)[d4];
-  }
-  const int n = hs.n;
-  const Plan p = make_plan(lo, n, a.band, S);
   const int npart = p.n_pre + p.n_post;
 
-  // ---- round 2: the reused state (the ring stores natural-log m and
-  // normalized o)
-  float2 rml = {neg_inf(), 0.f};
-  float4 ro = {0.f, 0.f, 0.f, 0.f};
-  const size_t re = (size_t)bh * R.slots + (hs.hit ? hs.slot : 0);
-  if (hs.hit) {
-    rml = reinterpret_cast<const float2*>(R.ml)[re];
-    ro = reinterpret_cast<const float4*>(R.o + re * D)[d4];
-  }
-
-  // ---- maxima of the slices before and after p_new
-  float mp = neg_inf(), mq = neg_inf();
+  // ---- round 1
+  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + DL * lane;
+  T qv[DL];
 #pragma unroll
-  for (int u = 0; u < kMl; ++u) {
-    const int k = tid + 256 * u;
-    if (k < npart) {
-      sw[k] = mlk[u].x;
-      sl[k] = mlk[u].y;
-      if (slice_is_pre(p, k)) mp = fmaxf(mp, mlk[u].x);
-      else mq = fmaxf(mq, mlk[u].x);
-    }
+  for (int e = 0; e < DL; ++e) qv[e] = qsrc[e];
+  float ob[kBatch][DL];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int k = u < S ? u : S - 1;
+    const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) ob[u][e] = src[e];
   }
-  mp = wave_max(mp);
-  mq = wave_max(mq);
-  if (lane == 0) {
-    red[0][wave] = mp;
-    red[1][wave] = mq;
+  for (int k = lane; k < S; k += 64) {
+    const float2 v = reinterpret_cast<const float2*>(a.part.ml)[pbase + (size_t)k * G];
+    sm[k] = v.x;
+    sl[k] = v.y;
   }
-  __syncthreads();
-  const float MA = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  const float MC = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
 
-  // ---- weights relative to each side's own maximum
+  // ---- round 2: the reused state (the ring stores natural-log m and
+  // normalized o).  Loaded unconditionally (slot 0 on a miss, which may
+  // never have been written) and selected on the hit, so no branch joins
+  // in front of the reductions.
+  const size_t re = (size_t)bh * R.slots + (hs.hit ? hs.slot : 0);
+  const float2 rml = reinterpret_cast<const float2*>(R.ml)[re];
+  float ro[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) ro[e] = R.o[re * D + DL * lane + e];
+
+  // ---- maxima of the slices before and after p_new, then weights relative
+  // to each side's own maximum
+  float mp = neg_inf(), mq = neg_inf();
+  for (int k = lane; k < npart; k += 64) {
+    if (slice_is_pre(p, k)) mp = fmaxf(mp, sm[k]);
+    else mq = fmaxf(mq, sm[k]);
+  }
+  const float MA = wave_max(mp), MC = wave_max(mq);
   float lp = 0.f, lq = 0.f;
-  for (int k = tid; k < npart; k += 256) {
+  for (int k = lane; k < npart; k += 64) {
     const bool pre = slice_is_pre(p, k);
-    const float mk = sw[k];
+    const float mk = sm[k];
     const float w = mk == neg_inf() ? 0.f : fast_exp2(mk - (pre ? MA : MC));
-    sw[k] = w;
+    sm[k] = w;
     if (pre) lp += w * sl[k];
     else lq += w * sl[k];
   }
-  lp = wave_sum(lp);
-  lq = wave_sum(lq);
-  if (lane == 0) {
-    red[2][wave] = lp;
-    red[3][wave] = lq;
-  }
-  __syncthreads();
-  const float LA = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
-  const float LC = (red[3][0] + red[3][1]) + (red[3][2] + red[3][3]);
+  const float LA = wave_sum(lp), LC = wave_sum(lq);
 
-  // ---- o of both sides (unnormalized, relative to MA and MC)
-  float4 op = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = sub; k0 < npart; k0 += NSUB * kBatch) {
-    float4 v[kBatch];
-    if (k0 == sub) {
+  // ---- o of both sides (unnormalized, relative to MA and MC), slice order
+  float oa[DL], oc[DL];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = v0[u];
-    } else {
+  for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
+  for (int k0 = 0; k0 < npart; k0 += kBatch) {
+    float cur[kBatch][DL];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int k = min(k0 + u * NSUB, S - 1);
-        v[u] = reinterpret_cast<const float4*>(a.part.o + (pbase + (size_t)k * G) * D)[d4];
+    for (int u = 0; u < kBatch; ++u) {
+      if (k0 == 0) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) cur[u][e] = ob[u][e];
+      } else {
+        const int k = k0 + u < S ? k0 + u : S - 1;
+        const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) cur[u][e] = src[e];
       }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int k = k0 + u * NSUB;
+      const int k = k0 + u;
       if (k < npart) {
-        const float w = sw[k];
+        const float w = sm[k];
         if (slice_is_pre(p, k)) {
-          op.x += w * v[u].x; op.y += w * v[u].y; op.z += w * v[u].z; op.w += w * v[u].w;
+#pragma unroll
+          for (int e = 0; e < DL; ++e) oa[e] += w * cur[u][e];
         } else {
-          oq.x += w * v[u].x; oq.y += w * v[u].y; oq.z += w * v[u].z; oq.w += w * v[u].w;
+#pragma unroll
+          for (int e = 0; e < DL; ++e) oc[e] += w * cur[u][e];
         }
       }
     }
-  }
-  rp[sub][d4] = op;
-  rq[sub][d4] = oq;
-  __syncthreads();
-  if (sub != 0) return;
-  float4 oa = {0.f, 0.f, 0.f, 0.f}, oc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    oa.x += rp[s][d4].x; oa.y += rp[s][d4].y; oa.z += rp[s][d4].z; oa.w += rp[s][d4].w;
-    oc.x += rq[s][d4].x; oc.y += rq[s][d4].y; oc.z += rq[s][d4].z; oc.w += rq[s][d4].w;
   }
 
   // ---- prefix = merge(reused, A), base 2
@@ -869,28 +823,28 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   const float sa = MA == neg_inf() ? 0.f : fast_exp2(MA - MP);
   const float LP = sr * lr + sa * LA;
   const float fr = sr * lr;
-  const float4 po = {fr * ro.x + sa * oa.x, fr * ro.y + sa * oa.y,
-                     fr * ro.z + sa * oa.z, fr * ro.w + sa * oa.w};
+  float po[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) po[e] = hs.hit ? fr * ro[e] + sa * oa[e] : sa * oa[e];
 
   // ---- the head's new ring entry: (q_pre, prefix state, p_new, n)
   const size_t we = (size_t)bh * R.slots + hs.cnt % R.slots;
-  const float4 eo = LP == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
-                              : float4{po.x / LP, po.y / LP, po.z / LP, po.w / LP};
-  reinterpret_cast<float4*>(R.o + we * D)[d4] = eo;
-  T* qdst = static_cast<T*>(R.q) + we * D + 4 * d4;
+  T* qdst = static_cast<T*>(R.q) + we * D + DL * lane;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) qdst[e] = qv[e];
+  for (int e = 0; e < DL; ++e) {
+    R.o[we * D + DL * lane + e] = LP == 0.f ? 0.f : po[e] / LP;
+    qdst[e] = qv[e];
+  }
 
   // ---- out = merge(prefix, C)
   const float M = fmaxf(MP, MC);
   const float sp = MP == neg_inf() ? 0.f : fast_exp2(MP - M);
   const float sc = MC == neg_inf() ? 0.f : fast_exp2(MC - M);
   const float den = sp * LP + sc * LC;
-  const float4 o4 = den == 0.f ? float4{0.f, 0.f, 0.f, 0.f}
-                               : float4{(sp * po.x + sc * oc.x) / den, (sp * po.y + sc * oc.y) / den,
-                                        (sp * po.z + sc * oc.z) / den, (sp * po.w + sc * oc.w) / den};
-  reinterpret_cast<float4*>(a.out + (size_t)bh * D)[d4] = o4;
-  if (d4 == 0) {
+#pragma unroll
+  for (int e = 0; e < DL; ++e)
+    a.out[(size_t)bh * D + DL * lane + e] = den == 0.f ? 0.f : (sp * po[e] + sc * oc[e]) / den;
+  if (lane == 0) {
     R.ml[we * 2] = LP == 0.f ? neg_inf() : MP * kLn2;
     R.ml[we * 2 + 1] = LP;
     R.pn[we * 2] = p.mid;
@@ -900,6 +854,26 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     // after the step kernel)
     if (a.k_new && h == 0) a.seq_lens[b] = n;
   }
+}
+
+// One wave per query head, a launch after the step kernel: the group's
+// match results come from the step kernel's records.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void merge_kernel(StepArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.hq, h = bh % a.hq;
+  const int G = a.group, kvh = h / G, hi = h % G;
+  const int grp = b * a.hkv + kvh;
+  const int lane = threadIdx.x;
+  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  __shared__ float sm[kMaxSlices];      // m, then the weight, of each slice
+  __shared__ float sl[kMaxSlices];
+  const HeadState hs = hsg[hi];
+  const int s_lane = hsg[lane < G ? lane : 0].s;        // G <= 16 lanes
+  int lo = hs.s;
+  for (int i = 0; i < G; ++i) lo = min(lo, __builtin_amdgcn_readlane(s_lane, i));
+  const Plan p = make_plan(lo, hs.n, a.band, a.part.S);
+  merge_head<T, D>(a, p, hs.n, hs, bh, grp, hi, lane, sm, sl);
 }
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
@@ -915,7 +889,7 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
   if (ev1) (void)hipEventRecord(ev1, st);
-#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq), dim3(256), 0, st, a)
+#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq), dim3(64), 0, st, a)
   MAC_DISPATCH(dtype, d, L_MERGE);
 #undef L_MERGE
   return hipGetLastError();
