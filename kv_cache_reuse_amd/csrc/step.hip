@@ -50,7 +50,9 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kMatchSlotsPerGroup = 16;   // ring slots per 16-lane group per round
+// ring slots per 16-lane group per round: a round covers 36 slots, so a
+// window of 32 (33 slots) takes one round with no padding loads to speak of
+constexpr int kMatchSlotsPerGroup = 9;
 constexpr int kPrefetch = MAC_ATTN_PREFETCH;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
@@ -115,8 +117,8 @@ struct MatchIn {
   static constexpr int EPL = D / 16;                       // elements per lane
   static constexpr int NW = EPL * (int)sizeof(T) / 4;      // dwords per lane
   uint32_t qw[NW];                          // this lane's piece of q_pre
-  uint32_t rw[kMatchSlotsPerGroup][NW];     // its piece of 16 ring rows
-  int2 pn[kMatchSlotsPerGroup];             // (p, n) of those slots
+  uint32_t rw[kMatchSlotsPerGroup][NW];     // its piece of the round's ring rows
+  int2 pnl;                                 // (p, n) of the round's slot `lane`
   double inv;                               // theta^(-2 lane / D)
   // rotate-half pair of this lane, widened to 32 bits: two 16-bit values
   // sharing a register would have to be packed, which waits for both loads
@@ -149,7 +151,8 @@ __device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[MatchIn<T, 
   }
 }
 
-// Ring slots s0 + gi + 4u (u < 16) of head bh.  Slot indices are clamped into
+// Ring slots s0 + gi + 4u (u < kMatchSlotsPerGroup) of head bh, and the
+// (p, n) of slot s0 + lane, one lane per slot.  Slot indices are clamped into
 // the ring; slots past W + 1 are dropped by the candidate test.
 template <typename T, int D>
 __device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, int s0,
@@ -158,12 +161,14 @@ __device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, 
   const int gi = lane / 16, c = lane % 16;
   const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
   const int2* rpn = reinterpret_cast<const int2*>(R.pn) + (size_t)bh * R.slots;
+  // (p, n) first: loads complete in order, and the candidate mask needs them
+  const int sl = s0 + lane;
+  mi.pnl = rpn[sl < R.slots ? sl : 0];
 #pragma unroll
   for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
     const int s = s0 + gi + 4 * u;
     const int sc = s < R.slots ? s : 0;
     load_row<T, D>(rq + (size_t)sc * D + c * MatchIn<T, D>::EPL, mi.rw[u]);
-    mi.pn[u] = rpn[sc];
   }
 }
 
@@ -222,7 +227,9 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
   // Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
   // candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
   // smallest squared distance, then smallest k (the newest entry).  The
-  // best entry's (p, n) travel with it, so no load follows the argmin.
+  // candidate test is taken one lane per slot and shared as a ballot mask;
+  // the best entry's (p, n) come from the lane of its slot, so no load
+  // follows the argmin.
   const int cnt = mi.cnt;
   const int nvalid = cnt < R.window ? cnt : R.window;
   // slot s is (r - s) mod (W + 1) steps old, r = (cnt - 1) mod (W + 1)
@@ -232,11 +239,17 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
   for (int e = 0; e < EPL; ++e) qv[e] = elem(mi.qw, e);
   float best = __builtin_inff();
   int bestk = -1, bp = 0, bn = -1;
+  auto age = [&](int s) { return s >= R.slots ? R.slots : (r >= s ? r - s : r - s + R.slots); };
   auto round = [&](int s0) {
+    const int sl = s0 + lane;
+    const int pl = mi.pnl.x;
+    const bool cl = lane < 4 * kMatchSlotsPerGroup && age(sl) < nvalid && pl >= 0 && pl <= p_new;
+    const uint64_t cmask = __ballot(cl);
+    int bj = -1;   // this round's best slot (index within the round) in this lane
 #pragma unroll
     for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
       if (s0 + 4 * u >= R.slots) break;   // the rest of the round is padding
-      const int s = s0 + gi + 4 * u;
+      const int j = gi + 4 * u;
       float d2 = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -244,16 +257,17 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
         d2 = fmaf(df, df, d2);
       }
       d2 = row16_sum(d2);
-      const int k = s >= R.slots ? R.slots : (r >= s ? r - s : r - s + R.slots);
-      const int pe = mi.pn[u].x;
-      const bool cand = k < nvalid && pe >= 0 && pe <= p_new && d2 == d2;
-      if (cand && (d2 < best || (d2 == best && k < bestk))) {
-        best = d2;
-        bestk = k;
-        bp = pe;
-        bn = mi.pn[u].y;
-      }
+      const int k = age(s0 + j);
+      const bool cand = ((cmask >> j) & 1) != 0 && d2 == d2;
+      const bool better = cand && (d2 < best || (d2 == best && k < bestk));
+      best = better ? d2 : best;
+      bestk = better ? k : bestk;
+      bj = better ? j : bj;
     }
+    const int px = __shfl(mi.pnl.x, bj >= 0 ? bj : 0, 64);
+    const int py = __shfl(mi.pnl.y, bj >= 0 ? bj : 0, 64);
+    bp = bj >= 0 ? px : bp;
+    bn = bj >= 0 ? py : bn;
   };
   // the first round straight-line: a loop header here would merge the
   // pending-load state and wait for every load in flight, the first tile's
