@@ -180,30 +180,34 @@ __host__ __device__ __forceinline__ Plan make_plan(int lo, int n, int band, int 
   return p;
 }
 
-__host__ __device__ __forceinline__ int split_bound(int a, int e, int n, int i) {
-  if (i <= 0) return a;
-  if (i >= n) return e;
-  // (e - a) * i / n; in 32 bits when the product fits (a 64-bit division is
-  // a long software sequence on the GPU)
-  const int64_t prod = int64_t(e - a) * i;
-  int x = a + (prod <= INT32_MAX ? static_cast<int>(static_cast<int32_t>(prod) / n)
-                                 : static_cast<int>(prod / n));
-  x &= ~(kTile - 1);
-  return x > a ? x : a;
+// Part i of [a, e) split into n parts on tile edges: the range's tiles
+// t0 .. t1 - 1 are dealt q = (t1 - t0) / n to each part and one more to the
+// first (t1 - t0) mod n parts; the first part starts at a and the last ends at
+// e.  One unsigned 32-bit division per call (the plan is computed before the
+// tile loop can start, where each instruction adds to the latency).  Every
+// part holds at least one tile when t1 - t0 >= n, which the slice counts of
+// make_plan guarantee.
+__host__ __device__ __forceinline__ void part_range(int a, int e, int n, int i, int* pa, int* pe) {
+  const unsigned t0 = static_cast<unsigned>(a) / kTile;
+  const unsigned nt = (static_cast<unsigned>(e) + kTile - 1) / kTile - t0;
+  const unsigned q = nt / static_cast<unsigned>(n), r = nt - q * static_cast<unsigned>(n);
+  auto bound = [&](int j) -> int {
+    if (j <= 0) return a;
+    if (j >= n) return e;
+    const unsigned uj = static_cast<unsigned>(j);
+    const int x = static_cast<int>((t0 + uj * q + (uj < r ? uj : r)) * kTile);
+    return x > a ? x : a;
+  };
+  *pa = bound(i);
+  *pe = bound(i + 1);
 }
 
 __host__ __device__ __forceinline__ bool slice_is_pre(const Plan& p, int i) { return i >= p.n_post; }
 
 // Key range [*a, *e) of slice i of a plan (i < n_pre + n_post).
 __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* a, int* e) {
-  if (i < p.n_post) {
-    *a = split_bound(p.mid, p.hi, p.n_post, i);
-    *e = split_bound(p.mid, p.hi, p.n_post, i + 1);
-  } else {
-    const int k = i - p.n_post;
-    *a = split_bound(p.lo, p.mid, p.n_pre, k);
-    *e = split_bound(p.lo, p.mid, p.n_pre, k + 1);
-  }
+  if (i < p.n_post) part_range(p.mid, p.hi, p.n_post, i, a, e);
+  else part_range(p.lo, p.mid, p.n_pre, i - p.n_post, a, e);
 }
 
 // Partial states: o unnormalized, m in log2 units of the scaled score.

@@ -341,6 +341,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const T* vc = static_cast<const T*>(a.v_cache);
   KvGeom geom = a.geom;
   geom.paged = PAGED ? 1 : 0;
+  geom.d = D;   // a compile-time tile size in the address arithmetic
   auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
     const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
