@@ -93,11 +93,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Row stride of the query rows in LDS: four elements of padding, so that the
+// 16 head columns of a fragment read fall in different banks.
+__host__ __device__ constexpr int qstride(int d) { return d + 4; }
+
 template <int D>
 struct Shared {
   HeadState head[kMaxGroup];
-  // rotated, scaled queries: bf16 hi/lo halves or fp32
-  __attribute__((aligned(16))) unsigned char q[2 * kMaxGroup * D * 2];
+  // rotated, scaled queries: bf16 hi/lo halves or fp32, rows of qstride(D)
+  // elements
+  __attribute__((aligned(16))) unsigned char q[kMaxGroup * qstride(D) * 4];
   // phase B epilogue: the four waves' states
   float m[4][kMaxGroup];
   float l[4][kMaxGroup];
@@ -210,15 +215,15 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
     const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
     const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
     if constexpr (sizeof(T) == 2) {
-      uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * D;
-      uint16_t* ql = reinterpret_cast<uint16_t*>(sh.q) + (kMaxGroup + hi) * D;
+      uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * qstride(D);
+      uint16_t* ql = reinterpret_cast<uint16_t*>(sh.q) + (kMaxGroup + hi) * qstride(D);
       const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
       qh[i] = h1;
       qh[i + D / 2] = h2;
       ql[i] = f32_to_bf16(r1 - bf16_to_f32(h1));
       ql[i + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
     } else {
-      float* qs = reinterpret_cast<float*>(sh.q) + hi * D;
+      float* qs = reinterpret_cast<float*>(sh.q) + hi * qstride(D);
       qs[i] = r1;
       qs[i + D / 2] = r2;
     }
@@ -435,8 +440,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     v4s qh[BF ? NQ : 1], ql[BF ? NQ : 1];
     float qf[BF ? 1 : NQ];
     if constexpr (BF) {
-      const uint16_t* qhs = reinterpret_cast<const uint16_t*>(sh.q) + col * D;
-      const uint16_t* qls = reinterpret_cast<const uint16_t*>(sh.q) + (kMaxGroup + col) * D;
+      const uint16_t* qhs = reinterpret_cast<const uint16_t*>(sh.q) + col * qstride(D);
+      const uint16_t* qls = reinterpret_cast<const uint16_t*>(sh.q) + (kMaxGroup + col) * qstride(D);
 #pragma unroll
       for (int j = 0; j < NL; ++j)
 #pragma unroll
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
           ql[2 * j + hh] = y;
         }
     } else {
-      const float* qss = reinterpret_cast<const float*>(sh.q) + col * D;
+      const float* qss = reinterpret_cast<const float*>(sh.q) + col * qstride(D);
 #pragma unroll
       for (int j = 0; j < NL; ++j)
 #pragma unroll
@@ -687,10 +692,12 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       sh.m[wave][col] = m;
       sh.l[wave][col] = lsum;
     }
+    if (hv) {   // padding columns are never read
 #pragma unroll
-    for (int i = 0; i < NCT; ++i)
+      for (int i = 0; i < NCT; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sh.o[wave][col][16 * i + 4 * lg + r] = acc[i][r];
+        for (int r = 0; r < 4; ++r) sh.o[wave][col][16 * i + 4 * lg + r] = acc[i][r];
+    }
     __syncthreads();
     const size_t pbase = ((size_t)grp * a.part.S + slice) * G;
     for (int idx = tid; idx < G * D; idx += 256) {
