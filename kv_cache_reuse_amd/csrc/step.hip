@@ -738,14 +738,16 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 // output.  No barrier: lane k takes the (m, l) of slices k, k + 64, ... (kept
 // in LDS for the wave, `sm`/`sl`), each lane owns D/64 output dims and folds
 // the slices' o in slice order with the weights read back from LDS, so
-// results are bitwise reproducible.  One round of loads brings every
-// slice's (m, l), the first kBatch slices' o and the query the entry copies
-// (slices the plan leaves unused hold stale values: read in bounds, never
-// used); the reused ring state follows in a second round that overlaps the
-// reductions and joins last as a two-way merge.
+// results are bitwise reproducible.  The first round of loads needs nothing
+// from the match records: every slice's (m, l) (first: loads complete in
+// order, and the reductions need these before any o), the query the entry
+// copies and the first kBatch slices' o (slices the plan leaves unused hold
+// stale values: read in bounds, never used).  The records come through
+// scalar loads alongside; the reused ring state, whose slot they name,
+// follows in a second round that overlaps the reductions and joins last as a
+// two-way merge.
 template <typename T, int D>
-__device__ __forceinline__ void merge_head(const StepArgs& a, const Plan& p, int n,
-                                           const HeadState& hs, int bh, int grp, int hi,
+__device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, int kvh, int hi,
                                            int lane, float* sm, float* sl) {
   constexpr int DL = D / 64;            // output dims per lane
   constexpr int kBatch = 32;            // slices whose o is loaded per round
@@ -753,9 +755,10 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, const Plan& p, int
   const int G = a.group, S = a.part.S;
   const RingView& R = a.ring;
   const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
-  const int npart = p.n_pre + p.n_post;
 
   // ---- round 1
+  const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
+  const float2 ml0 = pml[pbase + (size_t)(lane < S ? lane : S - 1) * G];
   const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + DL * lane;
   T qv[DL];
 #pragma unroll
@@ -768,8 +771,20 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, const Plan& p, int
 #pragma unroll
     for (int e = 0; e < DL; ++e) ob[u][e] = src[e];
   }
-  for (int k = lane; k < S; k += 64) {
-    const float2 v = reinterpret_cast<const float2*>(a.part.ml)[pbase + (size_t)k * G];
+  // the group's match records (uniform addresses: scalar loads) and the plan
+  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  const HeadState hs = hsg[hi];
+  int lo = hs.s;
+  for (int i = 0; i < G; ++i) lo = min(lo, hsg[i].s);
+  const int n = hs.n;
+  const Plan p = make_plan(lo, n, a.band, S);
+  const int npart = p.n_pre + p.n_post;
+  if (lane < S) {
+    sm[lane] = ml0.x;
+    sl[lane] = ml0.y;
+  }
+  for (int k = lane + 64; k < S; k += 64) {   // more than 64 slices
+    const float2 v = pml[pbase + (size_t)k * G];
     sm[k] = v.x;
     sl[k] = v.y;
   }
@@ -886,16 +901,9 @@ __global__ __launch_bounds__(64) void merge_kernel(StepArgs a) {
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group, kvh = h / G, hi = h % G;
   const int grp = b * a.hkv + kvh;
-  const int lane = threadIdx.x;
-  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
   __shared__ float sm[kMaxSlices];      // m, then the weight, of each slice
   __shared__ float sl[kMaxSlices];
-  const HeadState hs = hsg[hi];
-  const int s_lane = hsg[lane < G ? lane : 0].s;        // G <= 16 lanes
-  int lo = hs.s;
-  for (int i = 0; i < G; ++i) lo = min(lo, __builtin_amdgcn_readlane(s_lane, i));
-  const Plan p = make_plan(lo, hs.n, a.band, a.part.S);
-  merge_head<T, D>(a, p, hs.n, hs, bh, grp, hi, lane, sm, sl);
+  merge_head<T, D>(a, bh, grp, kvh, hi, threadIdx.x, sm, sl);
 }
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
