@@ -779,10 +779,8 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   const int n = hs.n;
   const Plan p = make_plan(lo, n, a.band, S);
   const int npart = p.n_pre + p.n_post;
-  if (lane < S) {
-    sm[lane] = ml0.x;
-    sl[lane] = ml0.y;
-  }
+  // the first 64 slices' (m, l) stay in registers (slice k in lane k); LDS
+  // holds the rest
   for (int k = lane + 64; k < S; k += 64) {   // more than 64 slices
     const float2 v = pml[pbase + (size_t)k * G];
     sm[k] = v.x;
@@ -802,13 +800,24 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   // ---- maxima of the slices before and after p_new, then weights relative
   // to each side's own maximum
   float mp = neg_inf(), mq = neg_inf();
-  for (int k = lane; k < npart; k += 64) {
+  if (lane < npart) {
+    if (slice_is_pre(p, lane)) mp = ml0.x;
+    else mq = ml0.x;
+  }
+  for (int k = lane + 64; k < npart; k += 64) {
     if (slice_is_pre(p, k)) mp = fmaxf(mp, sm[k]);
     else mq = fmaxf(mq, sm[k]);
   }
   const float MA = wave_max(mp), MC = wave_max(mq);
-  float lp = 0.f, lq = 0.f;
-  for (int k = lane; k < npart; k += 64) {
+  // weights: slice `lane` in w0, slices from 64 on in LDS
+  float lp = 0.f, lq = 0.f, w0 = 0.f;
+  if (lane < npart) {
+    const bool pre = slice_is_pre(p, lane);
+    w0 = ml0.x == neg_inf() ? 0.f : fast_exp2(ml0.x - (pre ? MA : MC));
+    if (pre) lp += w0 * ml0.y;
+    else lq += w0 * ml0.y;
+  }
+  for (int k = lane + 64; k < npart; k += 64) {
     const bool pre = slice_is_pre(p, k);
     const float mk = sm[k];
     const float w = mk == neg_inf() ? 0.f : fast_exp2(mk - (pre ? MA : MC));
@@ -817,30 +826,46 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
     else lq += w * sl[k];
   }
   const float LA = wave_sum(lp), LC = wave_sum(lq);
+  // slice k's weight for the fold: a lane read for k < 64 (no LDS round trip
+  // per slice), LDS beyond
+  auto weight = [&](int k) -> float {
+    return k < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), k)) : sm[k];
+  };
 
   // ---- o of both sides (unnormalized, relative to MA and MC), slice order
   float oa[DL], oc[DL];
 #pragma unroll
   for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
-  for (int k0 = 0; k0 < npart; k0 += kBatch) {
+  // the first kBatch slices: o from the first round, weights read from the
+  // lane that holds them (constant lane indices), straight-line
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    if (u < npart) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
+      if (slice_is_pre(p, u)) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) oa[e] += w * ob[u][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) oc[e] += w * ob[u][e];
+      }
+    }
+  }
+  // more slices: further rounds of kBatch
+  for (int k0 = kBatch; k0 < npart; k0 += kBatch) {
     float cur[kBatch][DL];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (k0 == 0) {
+      const int k = k0 + u < S ? k0 + u : S - 1;
+      const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) cur[u][e] = ob[u][e];
-      } else {
-        const int k = k0 + u < S ? k0 + u : S - 1;
-        const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) cur[u][e] = src[e];
-      }
+      for (int e = 0; e < DL; ++e) cur[u][e] = src[e];
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int k = k0 + u;
       if (k < npart) {
-        const float w = sm[k];
+        const float w = weight(k);
         if (slice_is_pre(p, k)) {
 #pragma unroll
           for (int e = 0; e < DL; ++e) oa[e] += w * cur[u][e];
