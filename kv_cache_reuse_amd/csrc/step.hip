@@ -11,12 +11,14 @@
 // Two launches per step, so that the only cross-workgroup hand-off goes
 // through a kernel boundary (no device-wide fences or atomics):
 //
-//  step_kernel, one 256-thread workgroup per (slice, KV group), slice-major,
-//  over a fixed number of slices S per group (the launch is the same for every
-//  step and can be captured in a graph):
+//  step_kernel, one workgroup per (slice, KV group), slice-major, over a
+//  fixed number of slices S per group (the launch is the same for every step
+//  and can be captured in a graph); 8 waves for groups of up to 4 query
+//  heads, 4 for wider ones:
 //   A. read the sequence length; for each of the group's G query heads rotate
 //      the query (float64 angles) and match the pre-RoPE query against the
-//      ring (one wave per head, 16 lanes per ring slot); derive the group's
+//      ring (two waves per head, each over half of its slots, or one wave per
+//      head for wide groups; 16 lanes per ring slot); derive the group's
 //      split-K plan and this workgroup's slice of keys.  The slice-0
 //      workgroup records every head's match result for the merge.
 //   B. with a non-empty slice: split-K attention on the matrix cores, one
@@ -24,9 +26,9 @@
 //      plan a miss would give is loaded while the match runs, and kept when
 //      the real plan gives the wave the same first tile (always on a miss,
 //      and for the slices after p_new on a hit); for the first slice before
-//      p_new one wave loads the tile a typical hit starts in instead.  With a fused append, the workgroup
-//      whose slice holds the new token stores it in the cache and patches it
-//      into the tile it loads.
+//      p_new one wave loads the tile a typical hit starts in instead.  With a
+//      fused append, the workgroup whose slice holds the new token stores it
+//      in the cache and patches it into the tile it loads.
 //  merge_kernel, one workgroup per query head: log-sum-exp merge of the
 //  reused state and the slices, the head's new ring entry and its output;
 //  with a fused append it also publishes the new length.
@@ -50,12 +52,21 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr float kLn2 = 0.69314718055994530942f;
-// ring slots per 16-lane group per round: a round covers 36 slots, so a
-// window of 32 (33 slots) takes one round with no padding loads to speak of
-constexpr int kMatchSlotsPerGroup = 9;
+// ring slots per 16-lane group per round.  A wave that takes all of a head's
+// slots covers 36 per round (a window of 32, 33 slots, in one round); two
+// waves that split a head's slots (even / odd) cover 20 each, 40 together.
+constexpr int kMatchSlotsWhole = 9;
+constexpr int kMatchSlotsHalf = 5;
 constexpr int kPrefetch = MAC_ATTN_PREFETCH;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Raw buffer descriptor over `bytes` bytes at p: no stride, 32-bit data
+// format (the word the gfx9 family takes for untyped buffer access).
+// Offsets past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 // Sum over each 16-lane row of the wave, result in every lane of the row:
@@ -97,32 +108,37 @@ __device__ __forceinline__ float wave_sum(float v) {
 // 16 head columns of a fragment read fall in different banks.
 __host__ __device__ constexpr int qstride(int d) { return d + 4; }
 
-template <int D>
+template <int D, int NE, int OC>
 struct Shared {
   HeadState head[kMaxGroup];
   // rotated, scaled queries: bf16 hi/lo halves or fp32, rows of qstride(D)
   // elements
   __attribute__((aligned(16))) unsigned char q[kMaxGroup * qstride(D) * 4];
-  // phase B epilogue: the four waves' states
-  float m[4][kMaxGroup];
-  float l[4][kMaxGroup];
-  float o[4][kMaxGroup][D + 1];
+  // match: each half of a head's ring slots' best candidate (d2 bits, age,
+  // p, n, pushes), combined after the match
+  int half_best[2][kMaxGroup][5];
+  // phase B epilogue: the streaming waves' states (OC head columns)
+  float m[NE][kMaxGroup];
+  float l[NE][kMaxGroup];
+  float o[NE][OC][D + 1];
   // fused append: the new token's key and value
   __attribute__((aligned(16))) unsigned char patch[2 * D * 4];
 };
 
 // =========================================================== phase A ====
-// One wave matches one query head h (index hi in the group).  The loads do
-// not depend on the sequence length, so they are issued first (match_load)
-// and the length is read while they are in flight; match_compute then
-// rotates the query and picks the best ring entry.  16 lanes share one ring
-// slot, each lane holding D/16 elements of the row; a round covers 64 slots.
-template <typename T, int D>
+// A wave matches one query head h (index hi in the group) over the ring
+// slots off, off + st, off + 2 st, ... (st = 2 splits a head's slots between
+// two waves).  The loads do not depend on the sequence length, so they are
+// issued first (match_load) and the length is read while they are in
+// flight; match_best then picks the best ring entry.  16 lanes share one
+// ring slot, each lane holding D/16 elements of the row; a round covers
+// 4 KMS slots.
+template <typename T, int D, int KMS>
 struct MatchIn {
   static constexpr int EPL = D / 16;                       // elements per lane
   static constexpr int NW = EPL * (int)sizeof(T) / 4;      // dwords per lane
   uint32_t qw[NW];                          // this lane's piece of q_pre
-  uint32_t rw[kMatchSlotsPerGroup][NW];     // its piece of the round's ring rows
+  uint32_t rw[KMS][NW];                     // its piece of the round's ring rows
   int2 pnl;                                 // (p, n) of the round's slot `lane`
   double inv;                               // theta^(-2 lane / D)
   // rotate-half pair of this lane, widened to 32 bits: two 16-bit values
@@ -140,8 +156,8 @@ template <> __device__ __forceinline__ float from_bits<float>(uint32_t w) { retu
 // a lane's D/16 elements of one row as 2, 4 or 8 dwords, one vector load
 // (rows start 16-byte aligned, so the lane's piece is aligned too)
 template <typename T, int D>
-__device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[MatchIn<T, D>::NW]) {
-  constexpr int NW = MatchIn<T, D>::NW;
+__device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[D / 16 * (int)sizeof(T) / 4]) {
+  constexpr int NW = D / 16 * (int)sizeof(T) / 4;
   if constexpr (NW == 2) {
     const u2 v = *reinterpret_cast<const u2*>(src);
     w[0] = v.x; w[1] = v.y;
@@ -156,57 +172,48 @@ __device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[MatchIn<T, 
   }
 }
 
-// Ring slots s0 + gi + 4u (u < kMatchSlotsPerGroup) of head bh, and the
-// (p, n) of slot s0 + lane, one lane per slot.  Slot indices are clamped into
+// Ring slots s0 + st (gi + 4u) + off (u < KMS) of head bh, and the (p, n) of
+// slot s0 + st lane + off, one lane per slot.  Slot indices are clamped into
 // the ring; slots past W + 1 are dropped by the candidate test.
-template <typename T, int D>
-__device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, int s0,
-                                           MatchIn<T, D>& mi) {
+template <typename T, int D, int KMS>
+__device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, int s0, int st,
+                                           int off, MatchIn<T, D, KMS>& mi) {
   const RingView& R = a.ring;
   const int gi = lane / 16, c = lane % 16;
   const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
   const int2* rpn = reinterpret_cast<const int2*>(R.pn) + (size_t)bh * R.slots;
   // (p, n) first: loads complete in order, and the candidate mask needs them
-  const int sl = s0 + lane;
+  const int sl = s0 + st * lane + off;
   mi.pnl = rpn[sl < R.slots ? sl : 0];
 #pragma unroll
-  for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
-    const int s = s0 + gi + 4 * u;
+  for (int u = 0; u < KMS; ++u) {
+    const int s = s0 + st * (gi + 4 * u) + off;
     const int sc = s < R.slots ? s : 0;
-    load_row<T, D>(rq + (size_t)sc * D + c * MatchIn<T, D>::EPL, mi.rw[u]);
+    load_row<T, D>(rq + (size_t)sc * D + c * MatchIn<T, D, KMS>::EPL, mi.rw[u]);
   }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, MatchIn<T, D>& mi) {
+template <typename T, int D, int KMS>
+__device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, int st, int off,
+                                           MatchIn<T, D, KMS>& mi) {
   const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
   const bool rot = lane < D / 2;
   mi.cnt = a.ring.count[bh];
   mi.inv = rot ? a.inv_freq[lane] : 0.0;
   mi.q1 = rot ? bits_of(q[lane]) : 0u;
   mi.q2 = rot ? bits_of(q[lane + D / 2]) : 0u;
-  load_row<T, D>(q + (lane % 16) * MatchIn<T, D>::EPL, mi.qw);
-  load_slots<T, D>(a, bh, lane, 0, mi);
+  load_row<T, D>(q + (lane % 16) * MatchIn<T, D, KMS>::EPL, mi.qw);
+  load_slots<T, D, KMS>(a, bh, lane, 0, st, off, mi);
 }
 
-// With write false the wave only consumes its loads (a wave past the
-// group's heads): loads left unread make the compiler wait for every load in
-// flight before their registers are reused.
-template <typename T, int D>
-__device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, int bh, int hi,
-                                              int lane, int n, int p_new, MatchIn<T, D>& mi,
-                                              bool write = true) {
-  constexpr int EPL = MatchIn<T, D>::EPL;
-  const int gi = lane / 16;
-  const RingView& R = a.ring;
-  auto elem = [&](const uint32_t (&w)[MatchIn<T, D>::NW], int e) -> float {
-    if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
-    else return __uint_as_float(w[e]);
-  };
-
-  // rotate-half pairs (i, i + D/2): float64 angle and rotation, result scaled
-  // by log2(e)/sqrt(D) so that the attention can use exp2
-  if (write && lane < D / 2) {
+// Rotate-half pairs (i, i + D/2) of head hi's query: float64 angle and
+// rotation, result scaled by log2(e)/sqrt(D) so that the attention can use
+// exp2; pairs i0 <= i < i1 are stored in LDS as bf16 hi/lo halves (or fp32).
+// Every lane that loaded a pair computes it, so the loads are consumed.
+template <typename T, int D, int KMS, class SH>
+__device__ __forceinline__ void rope_q(SH& sh, int hi, int lane, int n, const MatchIn<T, D, KMS>& mi,
+                                       int i0 = 0, int i1 = D / 2) {
+  if (lane < D / 2) {
     const int i = lane;
     double sn, cs;
     sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
@@ -214,6 +221,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
     const double sc = kLog2e / sqrt(static_cast<double>(D));
     const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
     const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
+    if (i < i0 || i >= i1) return;
     if constexpr (sizeof(T) == 2) {
       uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * qstride(D);
       uint16_t* ql = reinterpret_cast<uint16_t*>(sh.q) + (kMaxGroup + hi) * qstride(D);
@@ -228,13 +236,38 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
       qs[i + D / 2] = r2;
     }
   }
+}
 
-  // Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
-  // candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
-  // smallest squared distance, then smallest k (the newest entry).  The
-  // candidate test is taken one lane per slot and shared as a ballot mask;
-  // the best entry's (p, n) come from the lane of its slot, so no load
-  // follows the argmin.
+// Best ring entry among this wave's slots: d2 = dist^2 (+inf if none),
+// k = its age (-1 if none), (p, n) of the entry.
+struct Best {
+  float d2;
+  int k, p, n;
+};
+
+// the better of two candidates: smaller distance, then the newer entry
+__device__ __forceinline__ bool better_than(float d2, int k, float bd2, int bk) {
+  return k >= 0 && (bk < 0 || d2 < bd2 || (d2 == bd2 && k < bk));
+}
+
+// Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
+// candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
+// smallest squared distance, then smallest k (the newest entry).  The
+// candidate test is taken one lane per slot and shared as a ballot mask; the
+// best entry's (p, n) come from the lane of its slot, so no load follows the
+// argmin.  Every wave consumes its loads (a wave past the group's heads
+// too): loads left unread make the compiler wait for every load in flight
+// before their registers are reused.
+template <typename T, int D, int KMS>
+__device__ __forceinline__ Best match_best(const StepArgs& a, int bh, int lane, int p_new, int st,
+                                           int off, MatchIn<T, D, KMS>& mi) {
+  constexpr int EPL = MatchIn<T, D, KMS>::EPL;
+  const int gi = lane / 16;
+  const RingView& R = a.ring;
+  auto elem = [&](const uint32_t (&w)[MatchIn<T, D, KMS>::NW], int e) -> float {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
+    else return __uint_as_float(w[e]);
+  };
   const int cnt = mi.cnt;
   const int nvalid = cnt < R.window ? cnt : R.window;
   // slot s is (r - s) mod (W + 1) steps old, r = (cnt - 1) mod (W + 1)
@@ -246,14 +279,14 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
   int bestk = -1, bp = 0, bn = -1;
   auto age = [&](int s) { return s >= R.slots ? R.slots : (r >= s ? r - s : r - s + R.slots); };
   auto round = [&](int s0) {
-    const int sl = s0 + lane;
+    const int sl = s0 + st * lane + off;
     const int pl = mi.pnl.x;
-    const bool cl = lane < 4 * kMatchSlotsPerGroup && age(sl) < nvalid && pl >= 0 && pl <= p_new;
+    const bool cl = lane < 4 * KMS && age(sl) < nvalid && pl >= 0 && pl <= p_new;
     const uint64_t cmask = __ballot(cl);
     int bj = -1;   // this round's best slot (index within the round) in this lane
 #pragma unroll
-    for (int u = 0; u < kMatchSlotsPerGroup; ++u) {
-      if (s0 + 4 * u >= R.slots) break;   // the rest of the round is padding
+    for (int u = 0; u < KMS; ++u) {
+      if (s0 + st * 4 * u + off >= R.slots) break;   // the rest of the round is padding
       const int j = gi + 4 * u;
       float d2 = 0.f;
 #pragma unroll
@@ -262,7 +295,7 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
         d2 = fmaf(df, df, d2);
       }
       d2 = row16_sum(d2);
-      const int k = age(s0 + j);
+      const int k = age(s0 + st * j + off);
       const bool cand = ((cmask >> j) & 1) != 0 && d2 == d2;
       const bool better = cand && (d2 < best || (d2 == best && k < bestk));
       best = better ? d2 : best;
@@ -277,58 +310,69 @@ __device__ __forceinline__ void match_compute(const StepArgs& a, Shared<D>& sh, 
   // the first round straight-line: a loop header here would merge the
   // pending-load state and wait for every load in flight, the first tile's
   // included
-  // (the second round too, for windows of 64 .. 127; a loop takes the rest)
-  constexpr int kRound = 4 * kMatchSlotsPerGroup;
+  // (the second round too; a loop takes the rest)
+  const int round_step = st * 4 * KMS;
   round(0);
-  if (R.slots > kRound) {
-    load_slots<T, D>(a, bh, lane, kRound, mi);
-    round(kRound);
+  if (round_step + off < R.slots) {
+    load_slots<T, D, KMS>(a, bh, lane, round_step, st, off, mi);
+    round(round_step);
   }
-  for (int s0 = 2 * kRound; s0 < R.slots; s0 += kRound) {
-    load_slots<T, D>(a, bh, lane, s0, mi);
+  for (int s0 = 2 * round_step; s0 + off < R.slots; s0 += round_step) {
+    load_slots<T, D, KMS>(a, bh, lane, s0, st, off, mi);
     round(s0);
   }
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const float ob = shfl_xor_f(best, off);
-    const int ok = shfl_xor_i(bestk, off);
-    const int op = shfl_xor_i(bp, off);
-    const int on = shfl_xor_i(bn, off);
-    if (ok >= 0 && (bestk < 0 || ob < best || (ob == best && ok < bestk))) {
+  for (int xo = 16; xo <= 32; xo <<= 1) {
+    const float ob = shfl_xor_f(best, xo);
+    const int ok = shfl_xor_i(bestk, xo);
+    const int op = shfl_xor_i(bp, xo);
+    const int on = shfl_xor_i(bn, xo);
+    if (better_than(ob, ok, best, bestk)) {
       best = ob;
       bestk = ok;
       bp = op;
       bn = on;
     }
   }
-  if (write && lane == 0) {
-    const bool hit = bestk >= 0 && best < a.tau2;
-    HeadState hs;
-    hs.hit = hit ? 1 : 0;
-    hs.slot = hit ? (cnt - 1 - bestk) % R.slots : -1;
-    hs.s = hit ? bp : 0;
-    hs.cnt = cnt;
-    hs.match_n = hit ? bn : -1;
-    hs.dist = bestk >= 0 ? sqrtf(best) : __builtin_inff();
-    hs.n = n;
-    hs.pad = 0;
-    sh.head[hi] = hs;
-  }
+  return Best{best, bestk, bp, bn};
+}
+
+// The head's match record from its best entry.
+__device__ __forceinline__ HeadState head_record(const StepArgs& a, const Best& bst, int cnt, int n) {
+  const bool hit = bst.k >= 0 && bst.d2 < a.tau2;
+  HeadState hs;
+  hs.hit = hit ? 1 : 0;
+  hs.slot = hit ? (cnt - 1 - bst.k) % a.ring.slots : -1;
+  hs.s = hit ? bst.p : 0;
+  hs.cnt = cnt;
+  hs.match_n = hit ? bst.n : -1;
+  hs.dist = bst.k >= 0 ? sqrtf(bst.d2) : __builtin_inff();
+  hs.n = n;
+  hs.pad = 0;
+  return hs;
 }
 
 // ========================================================== the kernel ==
-// WIDE: groups of more than 4 query heads (each wave matches several); a
-// separate instantiation so that the narrow case's code has no conditional
-// loads (which make the compiler wait for every load in flight).
+// Narrow groups (at most 4 query heads): 8 waves; wave w matches head
+// w mod 4 over half of its ring slots (even slots for w < 4, odd for the
+// others), and the halves are combined after the match.  WIDE: groups of
+// more than 4 query heads, 4 waves, each matching several heads over all
+// their slots; a separate instantiation so that the narrow case's code has
+// no conditional loads (which make the compiler wait for every load in
+// flight).
 template <typename T, int D, bool PAGED, bool WIDE>
-__global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
+__global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
+  constexpr int NWV = WIDE ? 4 : 8;             // waves per workgroup
+  constexpr int NWB = 4;                        // waves that stream tiles
+  constexpr int NTH = 64 * NWV;
+  constexpr int KMS = WIDE ? kMatchSlotsWhole : kMatchSlotsHalf;
   constexpr bool BF = sizeof(T) == 2;
   constexpr int E = 16 / (int)sizeof(T);
   constexpr int NL = D * (int)sizeof(T) / 64;   // 1 KiB blocks per tile, K and V each
   constexpr int NQ = BF ? 2 * NL : 4 * NL;      // QK MFMA steps per tile
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
-  __shared__ Shared<D> sh;
+  __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
   const int n_groups = a.batch * a.hkv;
   const int grp = blockIdx.x % n_groups;
   const int slice = blockIdx.x / n_groups;
@@ -347,14 +391,21 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   KvGeom geom = a.geom;
   geom.paged = PAGED ? 1 : 0;
   geom.d = D;   // a compile-time tile size in the address arithmetic
+  // One tile's K and V through buffer loads: the tile's address goes into a
+  // buffer descriptor in scalar registers, and each lane's byte offset
+  // (16 lane + 1024 j) is the same for every tile, so no vector register is
+  // rewritten per tile (a per-tile vector address can land on a register
+  // that a load in flight still targets, and the compiler then waits for
+  // every load).  The descriptor covers exactly the tile.
+  const uint32_t loff = 16u * static_cast<uint32_t>(lane);
   auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
-    const u4* kp = reinterpret_cast<const u4*>(kc + base) + lane;
-    const u4* vp = reinterpret_cast<const u4*>(vc + base) + lane;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, kTile * D * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, kTile * D * (int)sizeof(T));
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kk[j] = kp[64 * j];
-      vv[j] = vp[64 * j];
+      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024u * j, 0, 0));
+      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024u * j, 0, 0));
     }
   };
 
@@ -362,12 +413,15 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   // the match loads of this wave's first head go out before the length
   // (waves past the group's heads load a valid head's rows and ignore them:
   // no branch, so the compiler need not wait for the loads at a join)
-  const int bh0 = b * a.hq + kvh * G + (wave < G ? wave : 0);
+  const int hi0 = WIDE ? wave : wave % 4;      // the wave's (first) head
+  const int half = WIDE ? 0 : wave / 4;        // narrow: which half of its slots
+  const int st = WIDE ? 1 : 2;                 // slot stride
+  const int bh0 = b * a.hq + kvh * G + (hi0 < G ? hi0 : 0);
   // groups wider than the 4 waves: a second buffer takes the wave's next
   // head right behind the first, and later heads are loaded one match ahead
-  MatchIn<T, D> mi[WIDE ? 2 : 1];
-  match_load<T, D>(a, bh0, lane, mi[0]);
-  if constexpr (WIDE) match_load<T, D>(a, wave + 4 < G ? bh0 + 4 : bh0, lane, mi[1]);
+  MatchIn<T, D, KMS> mi[WIDE ? 2 : 1];
+  match_load<T, D, KMS>(a, bh0, lane, st, half, mi[0]);
+  if constexpr (WIDE) match_load<T, D, KMS>(a, wave + 4 < G ? bh0 + 4 : bh0, lane, st, half, mi[1]);
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
@@ -379,7 +433,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   int ska = 0, ske = 0;
   if (slice < ps.n_pre + ps.n_post) slice_range(ps, slice, &ska, &ske);
   const int st0 = ska / kTile, st1 = (ske + kTile - 1) / kTile;
-  int tspec = st0 + wave < st1 ? st0 + wave : st1 - 1;
+  // (waves past the streaming ones load wave - NWB's tile: the same lines,
+  // an L2 hit, and every wave issues the same loads)
+  const int wb = wave % NWB;
+  int tspec = st0 + wb < st1 ? st0 + wb : st1 - 1;
   if (tspec < 0) tspec = 0;
   // On a hit the first slice before p_new usually holds only key p_new - 1
   // (a match one step old starts its band one key earlier): wave 0 of that
@@ -399,27 +456,60 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     pke = static_cast<const T*>(a.k_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
     pve = static_cast<const T*>(a.v_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
   }
-  match_compute<T, D>(a, sh, bh0, wave, lane, n, p_new, mi[0], wave < G);
   if constexpr (WIDE) {
-    // heads 4 r + wave, r = 1 .. 3, with the buffers chosen at compile time
+    // heads 4 r + wave, r = 0 .. 3, with the buffers chosen at compile time
+    if (hi0 < G) rope_q<T, D, KMS>(sh, hi0, lane, n, mi[0]);
+    {
+      const Best bst = match_best<T, D, KMS>(a, bh0, lane, p_new, st, half, mi[0]);
+      if (hi0 < G && lane == 0) sh.head[hi0] = head_record(a, bst, mi[0].cnt, n);
+    }
     auto more = [&](auto rc) {
       constexpr int r = decltype(rc)::value;
       const int hi = wave + 4 * r;
       if (hi < G) {
-        if (hi + 4 < G) match_load<T, D>(a, bh0 + 4 * (r + 1), lane, mi[(r + 1) & 1]);
-        match_compute<T, D>(a, sh, bh0 + 4 * r, hi, lane, n, p_new, mi[r & 1]);
+        if (hi + 4 < G) match_load<T, D, KMS>(a, bh0 + 4 * (r + 1), lane, st, half, mi[(r + 1) & 1]);
+        rope_q<T, D, KMS>(sh, hi, lane, n, mi[r & 1]);
+        const Best bst = match_best<T, D, KMS>(a, bh0 + 4 * r, lane, p_new, st, half, mi[r & 1]);
+        if (lane == 0) sh.head[hi] = head_record(a, bst, mi[r & 1].cnt, n);
       }
     };
     static_assert(kMaxGroup == 16, "four heads per wave at most");
     more(std::integral_constant<int, 1>{});
     more(std::integral_constant<int, 2>{});
     more(std::integral_constant<int, 3>{});
+  } else {
+    // both halves rotate the query, each storing half of the pairs: every
+    // wave consumes the rotation's loads (loads some path leaves unread make
+    // the compiler wait for every load in flight before their registers are
+    // reused, at the tile loop's head)
+    if (hi0 < G) rope_q<T, D, KMS>(sh, hi0, lane, n, mi[0], half * (D / 4), (half + 1) * (D / 4));
+    const Best bst = match_best<T, D, KMS>(a, bh0, lane, p_new, st, half, mi[0]);
+    if (hi0 < G && lane == 0) {
+      int* hb = sh.half_best[half][hi0];
+      hb[0] = __float_as_int(bst.d2);
+      hb[1] = bst.k;
+      hb[2] = bst.p;
+      hb[3] = bst.n;
+      hb[4] = mi[0].cnt;
+    }
   }
   if (early_patch && tid < D) {
     pk[tid] = pke;
     pv[tid] = pve;
   }
   __syncthreads();
+  if constexpr (!WIDE) {
+    // the two halves of each head's slots -> the head's record
+    if (wave == 0 && lane < G) {
+      const int* e0 = sh.half_best[0][lane];
+      const int* e1 = sh.half_best[1][lane];
+      Best bst{__int_as_float(e0[0]), e0[1], e0[2], e0[3]};
+      const float d1 = __int_as_float(e1[0]);
+      if (better_than(d1, e1[1], bst.d2, bst.k)) bst = Best{d1, e1[1], e1[2], e1[3]};
+      sh.head[lane] = head_record(a, bst, e0[4], n);
+    }
+    __syncthreads();
+  }
   int lo = sh.head[0].s, smax = sh.head[0].s;
   for (int i = 1; i < G; ++i) {
     lo = min(lo, sh.head[i].s);
@@ -474,7 +564,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     if (patcher && !early_patch) {
       const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.geom.hkv + kvr) * D;
       const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.geom.hkv + kvr) * D;
-      for (int e = tid; e < D; e += 256) {
+      for (int e = tid; e < D; e += NTH) {
         pk[e] = kn[e];
         pv[e] = vn[e];
       }
@@ -624,47 +714,50 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       }
     };
 
-    // Wave w takes tiles t0 + w, t0 + w + 4, ...; the next tiles are loaded
-    // while the current one is processed.  Prefetch loads are unconditional
+    // Wave w < NWB takes tiles t0 + w, t0 + w + NWB, ...; the next tiles are
+    // loaded
+    // while the current one is processed (with 8 waves, two per SIMD, the
+    // tile loop measured slower: waves past NWB only wait at the epilogue).
+    // Prefetch loads are unconditional
     // (an index past the slice is clamped to its last tile, an in-bounds
     // cache hit): a load under a branch leaves the outstanding-load count
     // unknown at the join, and the compiler then waits for every load,
     // prefetches included, before the current tile's math.
-    // nt tiles for this wave: t0 + wave, + 4, ...; pairs in a loop with one
+    // nt tiles for this wave: t0 + wave, + NWB, ...; pairs in a loop with one
     // exit (a loop left in the middle makes the compiler wait for every
     // load in flight at its header), then the odd one
     const int tlast = t1 - 1;
     const int tw = t0 + wave;
-    const int nt = tw < t1 ? (t1 - tw + 3) / 4 : 0;
+    const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
     if (nt > 0) {
       if constexpr (kPrefetch == 1) {
         u4 kB[NL], vB[NL];
         if (tw != tspec) load_tile(tw, kA, vA);
         int i = 0;
         for (; i + 1 < nt; i += 2) {
-          const int t = tw + 4 * i;
-          load_tile(t + 4, kB, vB);
+          const int t = tw + NWB * i;
+          load_tile(t + NWB, kB, vB);
           process(t, kA, vA);
-          load_tile(min(t + 8, tlast), kA, vA);
-          process(t + 4, kB, vB);
+          load_tile(min(t + 2 * NWB, tlast), kA, vA);
+          process(t + NWB, kB, vB);
         }
-        if (i < nt) process(tw + 4 * i, kA, vA);
+        if (i < nt) process(tw + NWB * i, kA, vA);
       } else {
         u4 kB[NL], vB[NL], kC[NL], vC[NL];
         if (tw != tspec) load_tile(tw, kA, vA);
-        load_tile(min(tw + 4, tlast), kB, vB);
+        load_tile(min(tw + NWB, tlast), kB, vB);
         int i = 0;
         for (; i + 2 < nt; i += 3) {
-          const int t = tw + 4 * i;
-          load_tile(t + 8, kC, vC);
+          const int t = tw + NWB * i;
+          load_tile(t + 2 * NWB, kC, vC);
           process(t, kA, vA);
-          load_tile(min(t + 12, tlast), kA, vA);
-          process(t + 4, kB, vB);
-          load_tile(min(t + 16, tlast), kB, vB);
-          process(t + 8, kC, vC);
+          load_tile(min(t + 3 * NWB, tlast), kA, vA);
+          process(t + NWB, kB, vB);
+          load_tile(min(t + 4 * NWB, tlast), kB, vB);
+          process(t + 2 * NWB, kC, vC);
         }
-        if (i < nt) process(tw + 4 * i, kA, vA);
-        if (i + 1 < nt) process(tw + 4 * i + 4, kB, vB);
+        if (i < nt) process(tw + NWB * i, kA, vA);
+        if (i + 1 < nt) process(tw + NWB * i + NWB, kB, vB);
       }
     }
     lsum += shfl_xor_f(lsum, 16);
@@ -687,12 +780,12 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       }
     }
 
-    // ---- the four waves' states -> the slice's partial state
-    if (lg == 0) {
+    // ---- the NWB streaming waves' states -> the slice's partial state
+    if (wave < NWB && lg == 0) {
       sh.m[wave][col] = m;
       sh.l[wave][col] = lsum;
     }
-    if (hv) {   // padding columns are never read
+    if (wave < NWB && hv) {   // padding columns are never read
 #pragma unroll
       for (int i = 0; i < NCT; ++i)
 #pragma unroll
@@ -700,14 +793,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
     __syncthreads();
     const size_t pbase = ((size_t)grp * a.part.S + slice) * G;
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < G * D; idx += NTH) {
       const int hh = idx / D, dim = idx % D;
       float Mx = sh.m[0][hh];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, sh.m[w][hh]);
+      for (int w = 1; w < NWB; ++w) Mx = fmaxf(Mx, sh.m[w][hh]);
       float o = 0.f, L = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NWB; ++w) {
         const float mw = sh.m[w][hh];
         const float sc = mw == neg_inf() ? 0.f : fast_exp2(mw - Mx);
         o += sc * sh.o[w][hh][dim];
@@ -938,9 +1031,9 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   const bool wide = a.group > 4;
 #define L_STEP(T, D)                                                                              \
   if (paged && wide) hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, a); \
-  else if (paged) hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(256), 0, st, a);  \
+  else if (paged) hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(512), 0, st, a);  \
   else if (wide) hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(256), 0, st, a);   \
-  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(256), 0, st, a)
+  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(512), 0, st, a)
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
   if (ev1) (void)hipEventRecord(ev1, st);
