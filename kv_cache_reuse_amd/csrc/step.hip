@@ -41,10 +41,6 @@
 #include "mac_dev.h"
 #include "mac_launch.h"
 
-#ifndef MAC_ATTN_PREFETCH
-#define MAC_ATTN_PREFETCH 1
-#endif
-
 namespace mac {
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -57,7 +53,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // waves that split a head's slots (even / odd) cover 20 each, 40 together.
 constexpr int kMatchSlotsWhole = 9;
 constexpr int kMatchSlotsHalf = 5;
-constexpr int kPrefetch = MAC_ATTN_PREFETCH;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -730,35 +725,17 @@ __global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
     const int tw = t0 + wave;
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
     if (nt > 0) {
-      if constexpr (kPrefetch == 1) {
-        u4 kB[NL], vB[NL];
-        if (tw != tspec) load_tile(tw, kA, vA);
-        int i = 0;
-        for (; i + 1 < nt; i += 2) {
-          const int t = tw + NWB * i;
-          load_tile(t + NWB, kB, vB);
-          process(t, kA, vA);
-          load_tile(min(t + 2 * NWB, tlast), kA, vA);
-          process(t + NWB, kB, vB);
-        }
-        if (i < nt) process(tw + NWB * i, kA, vA);
-      } else {
-        u4 kB[NL], vB[NL], kC[NL], vC[NL];
-        if (tw != tspec) load_tile(tw, kA, vA);
-        load_tile(min(tw + NWB, tlast), kB, vB);
-        int i = 0;
-        for (; i + 2 < nt; i += 3) {
-          const int t = tw + NWB * i;
-          load_tile(t + 2 * NWB, kC, vC);
-          process(t, kA, vA);
-          load_tile(min(t + 3 * NWB, tlast), kA, vA);
-          process(t + NWB, kB, vB);
-          load_tile(min(t + 4 * NWB, tlast), kB, vB);
-          process(t + 2 * NWB, kC, vC);
-        }
-        if (i < nt) process(tw + NWB * i, kA, vA);
-        if (i + 1 < nt) process(tw + NWB * i + NWB, kB, vB);
+      u4 kB[NL], vB[NL];
+      if (tw != tspec) load_tile(tw, kA, vA);
+      int i = 0;
+      for (; i + 1 < nt; i += 2) {
+        const int t = tw + NWB * i;
+        load_tile(t + NWB, kB, vB);
+        process(t, kA, vA);
+        load_tile(min(t + 2 * NWB, tlast), kA, vA);
+        process(t + NWB, kB, vB);
       }
+      if (i < nt) process(tw + NWB * i, kA, vA);
     }
     lsum += shfl_xor_f(lsum, 16);
     lsum += shfl_xor_f(lsum, 32);
