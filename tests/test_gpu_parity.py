@@ -69,6 +69,26 @@ def test_small_shapes_every_step(name):
     assert_report(rep, name, min_hits)
 
 
+@pytest.mark.parametrize("name,period", [("8b_32k", 3), ("70b_128k", 3), ("tiny", 2)])
+def test_exact_ties_take_the_newest_entry(name, period):
+    # q_t repeats q_{t-period} exactly, so several ring entries lie at
+    # distance 0 from the query: the newest must win on both sides.  With a
+    # period of 3 (or 2) the tied entries sit in ring slots of both
+    # parities, so for narrow groups they fall to the two waves that split a
+    # head's slots, and the cross-wave combine decides.  The harness would
+    # accept either entry of an exact tie as borderline; here none may occur.
+    kw = dict(context=700, steps=30, period=period, window=8, band=64)
+    if name != "tiny":
+        kw["batch"] = 1
+    w = workload(name, **kw)
+    say(f"[ties {name} period {period}] {w}")
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"ties_{name}", min_hits=(w.steps - 2 * period) * w.batch * w.n_q_heads)
+    assert not rep.borderline, rep.borderline[:5]
+
+
 @pytest.mark.parametrize("name", ["ctx1", "8b_32k_ragged", "paged_b8_small", "d64_bf16"])
 def test_stale_cache_slots_do_not_leak(name):
     # unwritten cache slots hold NaN; they sit past the end of each sequence
