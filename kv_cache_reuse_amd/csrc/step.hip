@@ -348,6 +348,13 @@ __device__ __forceinline__ HeadState head_record(const StepArgs& a, const Best& 
 }
 
 // ========================================================== the kernel ==
+// Waves per workgroup: 8, except for wide groups of fp32 d128 tiles, whose
+// registers do not fit two waves per SIMD (4 waves, up to four heads each).
+template <typename T, int D, bool WIDE>
+__host__ __device__ constexpr int step_waves() {
+  return WIDE && sizeof(T) == 4 && D == 128 ? 4 : 8;
+}
+
 // Narrow groups (at most 4 query heads): 8 waves; wave w matches head
 // w mod 4 over half of its ring slots (even slots for w < 4, odd for the
 // others), and the halves are combined after the match.  WIDE: groups of
@@ -356,8 +363,8 @@ __device__ __forceinline__ HeadState head_record(const StepArgs& a, const Best& 
 // no conditional loads (which make the compiler wait for every load in
 // flight).
 template <typename T, int D, bool PAGED, bool WIDE>
-__global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
-  constexpr int NWV = WIDE ? 4 : 8;             // waves per workgroup
+__global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
+  constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
   constexpr int NWB = 4;                        // waves that stream tiles
   constexpr int NTH = 64 * NWV;
   constexpr int KMS = WIDE ? kMatchSlotsWhole : kMatchSlotsHalf;
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
   // head right behind the first, and later heads are loaded one match ahead
   MatchIn<T, D, KMS> mi[WIDE ? 2 : 1];
   match_load<T, D, KMS>(a, bh0, lane, st, half, mi[0]);
-  if constexpr (WIDE) match_load<T, D, KMS>(a, wave + 4 < G ? bh0 + 4 : bh0, lane, st, half, mi[1]);
+  if constexpr (WIDE) match_load<T, D, KMS>(a, wave + NWV < G ? bh0 + NWV : bh0, lane, st, half, mi[1]);
   const int n0 = a.seq_lens[b];
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
     pve = static_cast<const T*>(a.v_new)[((size_t)b * a.geom.hkv + kvr) * D + tid];
   }
   if constexpr (WIDE) {
-    // heads 4 r + wave, r = 0 .. 3, with the buffers chosen at compile time
+    // heads NWV r + wave, with the buffers chosen at compile time
     if (hi0 < G) rope_q<T, D, KMS>(sh, hi0, lane, n, mi[0]);
     {
       const Best bst = match_best<T, D, KMS>(a, bh0, lane, p_new, st, half, mi[0]);
@@ -460,18 +467,20 @@ __global__ __launch_bounds__(WIDE ? 256 : 512) void step_kernel(StepArgs a) {
     }
     auto more = [&](auto rc) {
       constexpr int r = decltype(rc)::value;
-      const int hi = wave + 4 * r;
+      const int hi = wave + NWV * r;
       if (hi < G) {
-        if (hi + 4 < G) match_load<T, D, KMS>(a, bh0 + 4 * (r + 1), lane, st, half, mi[(r + 1) & 1]);
+        if (hi + NWV < G) match_load<T, D, KMS>(a, bh0 + NWV * (r + 1), lane, st, half, mi[(r + 1) & 1]);
         rope_q<T, D, KMS>(sh, hi, lane, n, mi[r & 1]);
-        const Best bst = match_best<T, D, KMS>(a, bh0 + 4 * r, lane, p_new, st, half, mi[r & 1]);
+        const Best bst = match_best<T, D, KMS>(a, bh0 + NWV * r, lane, p_new, st, half, mi[r & 1]);
         if (lane == 0) sh.head[hi] = head_record(a, bst, mi[r & 1].cnt, n);
       }
     };
-    static_assert(kMaxGroup == 16, "four heads per wave at most");
+    static_assert(kMaxGroup == 16 && (NWV == 8 || NWV == 4), "16 heads over the waves");
     more(std::integral_constant<int, 1>{});
-    more(std::integral_constant<int, 2>{});
-    more(std::integral_constant<int, 3>{});
+    if constexpr (NWV == 4) {
+      more(std::integral_constant<int, 2>{});
+      more(std::integral_constant<int, 3>{});
+    }
   } else {
     // both halves rotate the query, each storing half of the pairs: every
     // wave consumes the rotation's loads (loads some path leaves unread make
@@ -1007,10 +1016,13 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   const int grid = a.batch * a.hkv * a.part.S;
   const bool wide = a.group > 4;
 #define L_STEP(T, D)                                                                              \
-  if (paged && wide) hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, a); \
-  else if (paged) hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(512), 0, st, a);  \
-  else if (wide) hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(256), 0, st, a);   \
-  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(512), 0, st, a)
+  if (paged && wide)                                                                                 \
+    hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+  else if (paged)                                                                                    \
+    hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+  else if (wide)                                                                                     \
+    hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
   if (ev1) (void)hipEventRecord(ev1, st);
