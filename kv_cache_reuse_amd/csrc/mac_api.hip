@@ -35,8 +35,8 @@ mac_status ok() {
   return MAC_OK;
 }
 
-// Split-K workgroups a miss step aims for: one 256-thread workgroup per
-// compute unit of a 256-CU part.
+// Split-K workgroups a miss step aims for: one workgroup per compute unit
+// of a 256-CU part.
 constexpr int kTargetWorkgroups = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -358,10 +358,10 @@ __host__ __device__ constexpr int step_waves() {
 // Narrow groups (at most 4 query heads): 8 waves; wave w matches head
 // w mod 4 over half of its ring slots (even slots for w < 4, odd for the
 // others), and the halves are combined after the match.  WIDE: groups of
-// more than 4 query heads, 4 waves, each matching several heads over all
-// their slots; a separate instantiation so that the narrow case's code has
-// no conditional loads (which make the compiler wait for every load in
-// flight).
+// more than 4 query heads, each wave matching up to two heads (four with 4
+// waves) over all their slots; a separate instantiation so that the narrow
+// case's code has no conditional loads (which make the compiler wait for
+// every load in flight).  In both, four waves stream the tiles.
 template <typename T, int D, bool PAGED, bool WIDE>
 __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
   constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
@@ -419,7 +419,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   const int half = WIDE ? 0 : wave / 4;        // narrow: which half of its slots
   const int st = WIDE ? 1 : 2;                 // slot stride
   const int bh0 = b * a.hq + kvh * G + (hi0 < G ? hi0 : 0);
-  // groups wider than the 4 waves: a second buffer takes the wave's next
+  // groups wider than the waves: a second buffer takes the wave's next
   // head right behind the first, and later heads are loaded one match ahead
   MatchIn<T, D, KMS> mi[WIDE ? 2 : 1];
   match_load<T, D, KMS>(a, bh0, lane, st, half, mi[0]);
