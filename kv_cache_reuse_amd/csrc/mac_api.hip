@@ -46,7 +46,7 @@ struct Layout {
   // ring
   size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
   // workspace
-  size_t w_po, w_pml, w_heads, w_invf, w_out, w_save, ws_bytes;
+  size_t w_po, w_pml, w_heads, w_reuse, w_invf, w_out, w_save, ws_bytes;
   int slices;
   int64_t capacity;     // keys per sequence
   int tiles_per_seq;    // contiguous cache
@@ -137,6 +137,7 @@ Layout layout(const mac_config* c) {
   L.w_po = off;      off = align256(off + (size_t)groups * S * G * d * 4);
   L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
   L.w_heads = off;   off = align256(off + bh * sizeof(mac::HeadState));
+  L.w_reuse = off;   off = align256(off + bh * (d + 2) * 4);   // o rows, then (m, l) pairs
   L.w_invf = off;  off = align256(off + (d / 2) * 8);
   L.w_out = off;   off = align256(off + bh * d * 4);          // ring seeding: discarded outputs
   L.w_save = off;  off = align256(off + (size_t)c->batch * 4); // ring seeding: saved lengths
@@ -356,6 +357,8 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.match_ctx_out = nullptr;
   a.dist_out = nullptr;
   a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
+  a.reuse_o = reinterpret_cast<float*>(ctx->ws + L.w_reuse);
+  a.reuse_ml = a.reuse_o + (size_t)c.batch * c.n_q_heads * c.head_dim;
   a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
   a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
   a.part.S = L.slices;
@@ -405,9 +408,12 @@ mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, con
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (ctx->profiling && ctx->ev_used < 65536) {
     if (ctx->ev_used == ctx->events.size()) {
+      // timing only (read after the stream has been synchronized): no
+      // system-scope fence, whose cache write-back and invalidation would
+      // otherwise fall inside the timed interval
       hipEvent_t x, y;
-      hipError_t e = hipEventCreate(&x);
-      if (e == hipSuccess) e = hipEventCreate(&y);
+      hipError_t e = hipEventCreateWithFlags(&x, hipEventDisableSystemFence);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&y, hipEventDisableSystemFence);
       if (e != hipSuccess) return device_fail(ctx, e, "mac_decode_step: creating timing events");
       ctx->events.emplace_back(x, y);
     }

@@ -230,6 +230,8 @@ struct StepArgs {
   int32_t* match_ctx_out;   // nullable
   float* dist_out;          // nullable
   HeadState* heads;         // [batch*Hq] match results of the step
+  float* reuse_o;           // [batch*Hq][D] the matched entry's o (hit heads)
+  float* reuse_ml;          // [batch*Hq][2] its (m, l)
   PartialView part;
   RingView ring;
   KvGeom geom;

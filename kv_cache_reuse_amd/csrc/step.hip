@@ -809,6 +809,21 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     if (a.match_ctx_out) a.match_ctx_out[bh] = sh.head[tid].match_n;
     if (a.dist_out) a.dist_out[bh] = sh.head[tid].dist;
   }
+  // the hit heads' matched ring states, copied to rows of their own so that
+  // the merge kernel loads them in its first round instead of behind the
+  // records.  The group's last workgroup does it: on a hit its slice is
+  // usually empty, and when every head misses there is nothing to copy.
+  if (slice == a.part.S - 1) {
+    for (int idx = tid; idx < G * D; idx += NTH) {
+      const int hh = idx / D, dim = idx % D;
+      if (sh.head[hh].hit) {
+        const int bh = b * a.hq + kvh * G + hh;
+        const size_t re = (size_t)bh * a.ring.slots + sh.head[hh].slot;
+        a.reuse_o[(size_t)bh * D + dim] = a.ring.o[re * D + dim];
+        if (dim < 2) a.reuse_ml[(size_t)bh * 2 + dim] = a.ring.ml[re * 2 + dim];
+      }
+    }
+  }
 }
 
 // ========================================================= merge kernel ==
@@ -822,9 +837,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
 // order, and the reductions need these before any o), the query the entry
 // copies and the first kBatch slices' o (slices the plan leaves unused hold
 // stale values: read in bounds, never used).  The records come through
-// scalar loads alongside; the reused ring state, whose slot they name,
-// follows in a second round that overlaps the reductions and joins last as a
-// two-way merge.
+// scalar loads alongside, and the reused ring state of a hit head from the
+// row the step kernel copied it to, so every load goes out in one round; the
+// reused state joins last, as a two-way merge.
 template <typename T, int D>
 __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, int kvh, int hi,
                                            int lane, float* sm, float* sl) {
@@ -835,13 +850,20 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   const RingView& R = a.ring;
   const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
 
-  // ---- round 1
+  // ---- the loads (one round)
   const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
   const float2 ml0 = pml[pbase + (size_t)(lane < S ? lane : S - 1) * G];
   const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + DL * lane;
   T qv[DL];
 #pragma unroll
   for (int e = 0; e < DL; ++e) qv[e] = qsrc[e];
+  // the reused state (the ring stores natural-log m and normalized o), as
+  // the step kernel copied it for a hit head; stale otherwise, and then
+  // never selected
+  const float2 rml = reinterpret_cast<const float2*>(a.reuse_ml)[bh];
+  float ro[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) ro[e] = a.reuse_o[(size_t)bh * D + DL * lane + e];
   float ob[kBatch][DL];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
@@ -865,16 +887,6 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
     sm[k] = v.x;
     sl[k] = v.y;
   }
-
-  // ---- round 2: the reused state (the ring stores natural-log m and
-  // normalized o).  Loaded unconditionally (slot 0 on a miss, which may
-  // never have been written) and selected on the hit, so no branch joins
-  // in front of the reductions.
-  const size_t re = (size_t)bh * R.slots + (hs.hit ? hs.slot : 0);
-  const float2 rml = reinterpret_cast<const float2*>(R.ml)[re];
-  float ro[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) ro[e] = R.o[re * D + DL * lane + e];
 
   // ---- maxima of the slices before and after p_new, then weights relative
   // to each side's own maximum
