@@ -827,32 +827,53 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
 }
 
 // ========================================================= merge kernel ==
-// Merge of one query head (b, h) by one wave: log-sum-exp merge of the
+// Merge of one query head (b, h) by `nw` waves: log-sum-exp merge of the
 // reused state and the group's slices, the head's new ring entry and its
-// output.  No barrier: lane k takes the (m, l) of slices k, k + 64, ... (kept
-// in LDS for the wave, `sm`/`sl`), each lane owns D/64 output dims and folds
-// the slices' o in slice order with the weights read back from LDS, so
-// results are bitwise reproducible.  The first round of loads needs nothing
-// from the match records: every slice's (m, l) (first: loads complete in
-// order, and the reductions need these before any o), the query the entry
-// copies and the first kBatch slices' o (slices the plan leaves unused hold
-// stale values: read in bounds, never used).  The records come through
-// scalar loads alongside, and the reused ring state of a hit head from the
-// row the step kernel copied it to, so every load goes out in one round; the
-// reused state joins last, as a two-way merge.
-template <typename T, int D>
+// output.  Wave w takes the contiguous slices [k0, k1) of the group's S
+// (at most 64; lane j holds the (m, l) of slice k0 + j), and each lane owns
+// D/64 output dims.  A wave folds its slices' o in slice order, with each
+// side's (before and after p_new) weights taken relative to the wave's own
+// maximum; wave 0 then rescales and adds the waves' sums in wave order, so
+// results are bitwise reproducible, and with one wave the arithmetic is the
+// plain ordered fold.  The loads go out in one round (two for more than 32
+// slices per wave) and need nothing from the match records: the slices'
+// (m, l) first (loads complete in order, and the reductions need these
+// before any o), then the query the entry copies, the reused ring state as
+// the step kernel copied it for a hit head, and the slices' o (slices the
+// plan leaves unused hold stale values: read in bounds, never used).  The
+// records come through scalar loads alongside.
+constexpr int kMergeMaxWaves = 16;
+constexpr int kMergeBatch = 32;   // slices whose o one wave loads per round
+
+__host__ __device__ inline int merge_waves(int S) {
+  const int w = (S + kMergeBatch - 1) / kMergeBatch;
+  return w < kMergeMaxWaves ? w : kMergeMaxWaves;
+}
+
+template <int D>
+struct MergeShared {
+  float m[kMergeMaxWaves][2];           // per wave: max of the slices before / after p_new
+  float l[kMergeMaxWaves][2];
+  float o[kMergeMaxWaves][2][D];
+};
+
+template <typename T, int D, bool MW>
 __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, int kvh, int hi,
-                                           int lane, float* sm, float* sl) {
+                                           int wave, int nw, int lane, MergeShared<MW ? D : 1>& xs) {
   constexpr int DL = D / 64;            // output dims per lane
-  constexpr int kBatch = 32;            // slices whose o is loaded per round
+  constexpr int kBatch = kMergeBatch;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group, S = a.part.S;
   const RingView& R = a.ring;
   const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
+  const int spw = (S + nw - 1) / nw;
+  const int k0 = wave * spw;
+  const int k1 = k0 + spw < S ? k0 + spw : S;           // empty when k0 >= S
 
-  // ---- the loads (one round)
+  // ---- the loads
   const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
-  const float2 ml0 = pml[pbase + (size_t)(lane < S ? lane : S - 1) * G];
+  const int kl = k0 + lane < S ? k0 + lane : S - 1;
+  const float2 ml0 = pml[pbase + (size_t)kl * G];
   const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + DL * lane;
   T qv[DL];
 #pragma unroll
@@ -865,13 +886,19 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
 #pragma unroll
   for (int e = 0; e < DL; ++e) ro[e] = a.reuse_o[(size_t)bh * D + DL * lane + e];
   float ob[kBatch][DL];
+  auto load_o = [&](int kb) {
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int k = u < S ? u : S - 1;
-    const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = kb + u < S ? kb + u : S - 1;
+      const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
 #pragma unroll
-    for (int e = 0; e < DL; ++e) ob[u][e] = src[e];
-  }
+      for (int e = 0; e < DL; ++e) ob[u][e] = src[e];
+    }
+  };
+  // wave 0 loads its slices' o in the first round: on a hit its slices are
+  // the only live ones.  The other waves' slices are live only when the
+  // plan is long (a miss); they load once the plan is known.
+  if (wave == 0) load_o(k0);
   // the group's match records (uniform addresses: scalar loads) and the plan
   const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
   const HeadState hs = hsg[hi];
@@ -880,60 +907,37 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   const int n = hs.n;
   const Plan p = make_plan(lo, n, a.band, S);
   const int npart = p.n_pre + p.n_post;
-  // the first 64 slices' (m, l) stay in registers (slice k in lane k); LDS
-  // holds the rest
-  for (int k = lane + 64; k < S; k += 64) {   // more than 64 slices
-    const float2 v = pml[pbase + (size_t)k * G];
-    sm[k] = v.x;
-    sl[k] = v.y;
-  }
+  const int ke = k1 < npart ? k1 : npart;               // this wave's live slices: [k0, ke)
+  if (MW && wave != 0 && k0 < ke) load_o(k0);
 
-  // ---- maxima of the slices before and after p_new, then weights relative
-  // to each side's own maximum
+  // ---- this wave's maxima of the slices before and after p_new, then
+  // weights relative to them (slice k0 + j's weight in lane j)
+  const bool live = k0 + lane < ke;
+  const bool pre0 = slice_is_pre(p, k0 + lane);
   float mp = neg_inf(), mq = neg_inf();
-  if (lane < npart) {
-    if (slice_is_pre(p, lane)) mp = ml0.x;
+  if (live) {
+    if (pre0) mp = ml0.x;
     else mq = ml0.x;
   }
-  for (int k = lane + 64; k < npart; k += 64) {
-    if (slice_is_pre(p, k)) mp = fmaxf(mp, sm[k]);
-    else mq = fmaxf(mq, sm[k]);
-  }
-  const float MA = wave_max(mp), MC = wave_max(mq);
-  // weights: slice `lane` in w0, slices from 64 on in LDS
+  float MA = wave_max(mp), MC = wave_max(mq);
   float lp = 0.f, lq = 0.f, w0 = 0.f;
-  if (lane < npart) {
-    const bool pre = slice_is_pre(p, lane);
-    w0 = ml0.x == neg_inf() ? 0.f : fast_exp2(ml0.x - (pre ? MA : MC));
-    if (pre) lp += w0 * ml0.y;
+  if (live) {
+    w0 = ml0.x == neg_inf() ? 0.f : fast_exp2(ml0.x - (pre0 ? MA : MC));
+    if (pre0) lp += w0 * ml0.y;
     else lq += w0 * ml0.y;
   }
-  for (int k = lane + 64; k < npart; k += 64) {
-    const bool pre = slice_is_pre(p, k);
-    const float mk = sm[k];
-    const float w = mk == neg_inf() ? 0.f : fast_exp2(mk - (pre ? MA : MC));
-    sm[k] = w;
-    if (pre) lp += w * sl[k];
-    else lq += w * sl[k];
-  }
-  const float LA = wave_sum(lp), LC = wave_sum(lq);
-  // slice k's weight for the fold: a lane read for k < 64 (no LDS round trip
-  // per slice), LDS beyond
-  auto weight = [&](int k) -> float {
-    return k < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), k)) : sm[k];
-  };
+  float LA = wave_sum(lp), LC = wave_sum(lq);
 
-  // ---- o of both sides (unnormalized, relative to MA and MC), slice order
+  // ---- o of both sides (unnormalized, relative to MA and MC), slice order;
+  // weights read from the lane that holds them
   float oa[DL], oc[DL];
 #pragma unroll
   for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
-  // the first kBatch slices: o from the first round, weights read from the
-  // lane that holds them (constant lane indices), straight-line
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
-    if (u < npart) {
+    if (k0 + u < ke) {
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
-      if (slice_is_pre(p, u)) {
+      if (slice_is_pre(p, k0 + u)) {
 #pragma unroll
         for (int e = 0; e < DL; ++e) oa[e] += w * ob[u][e];
       } else {
@@ -942,28 +946,59 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
       }
     }
   }
-  // more slices: further rounds of kBatch
-  for (int k0 = kBatch; k0 < npart; k0 += kBatch) {
-    float cur[kBatch][DL];
+  // a wave's second round (more than 32 slices per wave)
+  if (k0 + kBatch < ke) {
+    load_o(k0 + kBatch);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int k = k0 + u < S ? k0 + u : S - 1;
-      const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
+      if (k0 + kBatch + u < ke) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), kBatch + u));
+        if (slice_is_pre(p, k0 + kBatch + u)) {
 #pragma unroll
-      for (int e = 0; e < DL; ++e) cur[u][e] = src[e];
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int k = k0 + u;
-      if (k < npart) {
-        const float w = weight(k);
-        if (slice_is_pre(p, k)) {
-#pragma unroll
-          for (int e = 0; e < DL; ++e) oa[e] += w * cur[u][e];
+          for (int e = 0; e < DL; ++e) oa[e] += w * ob[u][e];
         } else {
 #pragma unroll
-          for (int e = 0; e < DL; ++e) oc[e] += w * cur[u][e];
+          for (int e = 0; e < DL; ++e) oc[e] += w * ob[u][e];
         }
+      }
+    }
+  }
+
+  // ---- the waves' sums, rescaled to the largest maximum and added in wave
+  // order by wave 0
+  if constexpr (MW) {
+    if (lane == 0) {
+      xs.m[wave][0] = MA;
+      xs.m[wave][1] = MC;
+      xs.l[wave][0] = LA;
+      xs.l[wave][1] = LC;
+    }
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+      xs.o[wave][0][DL * lane + e] = oa[e];
+      xs.o[wave][1][DL * lane + e] = oc[e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    MA = xs.m[0][0];
+    MC = xs.m[0][1];
+    for (int w = 1; w < nw; ++w) {
+      MA = fmaxf(MA, xs.m[w][0]);
+      MC = fmaxf(MC, xs.m[w][1]);
+    }
+    LA = LC = 0.f;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float ma = xs.m[w][0], mc = xs.m[w][1];
+      const float sa = ma == neg_inf() ? 0.f : fast_exp2(ma - MA);
+      const float sc = mc == neg_inf() ? 0.f : fast_exp2(mc - MC);
+      LA += sa * xs.l[w][0];
+      LC += sc * xs.l[w][1];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) {
+        oa[e] += sa * xs.o[w][0][DL * lane + e];
+        oc[e] += sc * xs.o[w][1][DL * lane + e];
       }
     }
   }
@@ -1009,17 +1044,20 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   }
 }
 
-// One wave per query head, a launch after the step kernel: the group's
-// match results come from the step kernel's records.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void merge_kernel(StepArgs a) {
+// One workgroup of merge_waves(S) waves per query head, a launch after the
+// step kernel: the group's match results come from the step kernel's records.
+// MW: more than one wave (a separate instantiation, so the one-wave merge
+// keeps a one-wave register budget and has no exchange).
+template <typename T, int D, bool MW>
+__global__ __launch_bounds__(MW ? 64 * kMergeMaxWaves : 64) void merge_kernel(StepArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.group, kvh = h / G, hi = h % G;
   const int grp = b * a.hkv + kvh;
-  __shared__ float sm[kMaxSlices];      // m, then the weight, of each slice
-  __shared__ float sl[kMaxSlices];
-  merge_head<T, D>(a, bh, grp, kvh, hi, threadIdx.x, sm, sl);
+  const int wave = MW ? __builtin_amdgcn_readfirstlane(threadIdx.x / 64) : 0;
+  const int nw = MW ? blockDim.x / 64 : 1;
+  __shared__ MergeShared<MW ? D : 1> xs;
+  merge_head<T, D, MW>(a, bh, grp, kvh, hi, wave, nw, threadIdx.x % 64, xs);
 }
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
@@ -1038,7 +1076,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
   if (ev1) (void)hipEventRecord(ev1, st);
-#define L_MERGE(T, D) hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.batch * a.hq), dim3(64), 0, st, a)
+#define L_MERGE(T, D)                                                                              \
+  if (merge_waves(a.part.S) > 1)                                                                   \
+    hipLaunchKernelGGL((merge_kernel<T, D, true>), dim3(a.batch * a.hq), dim3(64 * merge_waves(a.part.S)), 0, st, a); \
+  else hipLaunchKernelGGL((merge_kernel<T, D, false>), dim3(a.batch * a.hq), dim3(64), 0, st, a)
   MAC_DISPATCH(dtype, d, L_MERGE);
 #undef L_MERGE
   return hipGetLastError();

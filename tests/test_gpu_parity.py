@@ -69,6 +69,20 @@ def test_small_shapes_every_step(name):
     assert_report(rep, name, min_hits)
 
 
+@pytest.mark.parametrize("max_slices", [100, 600, 1024])
+def test_merge_over_many_slices(max_slices):
+    # more slices per group than one merge wave folds: several waves per
+    # query head (100: four waves, the last one partly filled) and, above
+    # 512 slices, two rounds of loads per wave; the context fills every
+    # slice on a miss
+    w = workload("8b_32k", n_q_heads=4, n_kv_heads=2, context=66000, steps=12, p_jump=0.3)
+    say(f"[slices{max_slices}] {w}")
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp, max_slices=max_slices)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"slices{max_slices}")
+
+
 @pytest.mark.parametrize("name,period", [("8b_32k", 3), ("70b_128k", 3), ("tiny", 2)])
 def test_exact_ties_take_the_newest_entry(name, period):
     # q_t repeats q_{t-period} exactly, so several ring entries lie at
