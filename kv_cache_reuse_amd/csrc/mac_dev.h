@@ -210,6 +210,38 @@ __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* 
   else part_range(p.lo, p.mid, p.n_pre, i - p.n_post, a, e);
 }
 
+// Workgroup id -> (group, slice) of the step launch, and the grid size.
+// Ids run slice-major (group = id mod groups): the hardware deals ids
+// round-robin to the 8 XCDs, so with 8 groups every slice of a group shares
+// one XCD and its L2 holds the group's ring rows once.  Wide groups split
+// into nchunk chunks read the same keys in every chunk: their ids run
+// chunk-major, each chunk's run padded to a multiple of 8, so the chunks of
+// a slice share an XCD and its L2 reads of the slice's tiles.  Padding ids
+// return false.
+constexpr int kXcds = 8;
+
+__host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S) {
+  if (nchunk == 1) return groups * S;
+  const int per = groups / nchunk * S;
+  return nchunk * ((per + kXcds - 1) / kXcds * kXcds);
+}
+
+__host__ __device__ __forceinline__ bool step_coords(int id, int groups, int nchunk, int S,
+                                                     int* grp, int* slice) {
+  if (nchunk == 1) {
+    *grp = id % groups;
+    *slice = id / groups;
+    return true;
+  }
+  const int nreal = groups / nchunk;
+  const int per = nreal * S, run = (per + kXcds - 1) / kXcds * kXcds;
+  const int c = id / run, j = id % run;
+  if (j >= per) return false;
+  *grp = (j % nreal) * nchunk + c;
+  *slice = j / nreal;
+  return true;
+}
+
 // Partial states: o unnormalized, m in log2 units of the scaled score.
 struct PartialView {
   float* o;    // [groups][S][G][D]

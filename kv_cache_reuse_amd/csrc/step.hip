@@ -375,23 +375,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
   __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
-  const int n_groups = a.batch * a.hkv;
   int grp, slice;
-  if (a.nchunk == 1) {
-    grp = blockIdx.x % n_groups;
-    slice = blockIdx.x / n_groups;
-  } else {
-    // Chunks of a wide group read the same keys.  Ids run chunk-major, each
-    // chunk's run padded to a multiple of the 8 XCDs the ids are dealt to,
-    // so the chunks of a slice run on one XCD side by side and share its L2
-    // reads of the slice's tiles.
-    const int nreal = n_groups / a.nchunk;
-    const int per = nreal * a.part.S, run = (per + 7) / 8 * 8;
-    const int c = blockIdx.x / run, j = blockIdx.x % run;
-    if (j >= per) return;     // padding: the whole workgroup leaves before any barrier
-    grp = (j % nreal) * a.nchunk + c;
-    slice = j / nreal;
-  }
+  // (padding ids of a chunked group leave before any barrier)
+  if (!step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice)) return;
   const int b = grp / a.hkv, kvh = grp % a.hkv;
   const int kvr = kvh / a.nchunk;          // the KV head whose cache is read
   const int G = a.group;
@@ -1077,8 +1063,7 @@ __global__ __launch_bounds__(MW ? 64 * kMergeMaxWaves : 64) void merge_kernel(St
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0) (void)hipEventRecord(ev0, st);
-  const int grid = a.nchunk == 1 ? a.batch * a.hkv * a.part.S
-                                  : a.nchunk * ((a.batch * a.hkv / a.nchunk * a.part.S + 7) / 8 * 8);
+  const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
 #define L_STEP(T, D)                                                                              \
   if (paged && wide)                                                                                 \

@@ -87,6 +87,37 @@ void check_plan(int lo, int n, int band, int S) {
   CHECK(cur == (p.n_post ? p.hi : p.mid), "slices end at %d", cur);
 }
 
+// Every (group, slice) of the step launch gets exactly one workgroup id;
+// padding ids are the only ones left over; the chunks of a wide group's
+// slice share an XCD (ids congruent mod 8).
+void check_coords(int groups, int nchunk, int S) {
+  const int grid = mac::step_grid(groups, nchunk, S);
+  std::vector<int> seen((size_t)groups * S, 0), xcd((size_t)groups * S, -1);
+  int pad = 0;
+  for (int id = 0; id < grid; ++id) {
+    int g = -1, s = -1;
+    if (!mac::step_coords(id, groups, nchunk, S, &g, &s)) {
+      ++pad;
+      continue;
+    }
+    CHECK(g >= 0 && g < groups && s >= 0 && s < S, "id %d -> (%d, %d) out of range (G %d C %d S %d)",
+          id, g, s, groups, nchunk, S);
+    if (g < 0 || g >= groups || s < 0 || s >= S) continue;
+    seen[(size_t)g * S + s]++;
+    xcd[(size_t)g * S + s] = id % mac::kXcds;
+  }
+  for (size_t i = 0; i < seen.size(); ++i)
+    CHECK(seen[i] == 1, "(group %zu, slice %zu) taken %d times (G %d C %d S %d)", i / S, i % S,
+          seen[i], groups, nchunk, S);
+  CHECK(pad < nchunk * mac::kXcds, "%d padding ids", pad);
+  if (nchunk > 1)
+    for (int g = 0; g < groups; ++g)
+      for (int s = 0; s < S; ++s) {
+        const int first = xcd[(size_t)(g - g % nchunk) * S + s];
+        CHECK(xcd[(size_t)g * S + s] == first, "chunks of group %d slice %d on different XCDs", g, s);
+      }
+}
+
 int main() {
   check_tiles<uint16_t>(64);
   check_tiles<uint16_t>(128);
@@ -102,6 +133,11 @@ int main() {
     int S = Ss[rng() % 7];
     check_plan(lo, n, band, S);
   }
+  for (int groups : {1, 2, 3, 8, 16, 64})
+    for (int S : {2, 5, 32, 128, 1024}) check_coords(groups, 1, S);
+  for (int real : {1, 2, 3, 8})
+    for (int nc : {2, 3, 4})
+      for (int S : {2, 5, 13, 64, 128}) check_coords(real * nc, nc, S);
   check_plan(0, 131072 + 512, 256, 128);
   check_plan(131072 + 300 - 256 - 1, 131072 + 300, 256, 128);
   if (fails) {
