@@ -11,16 +11,17 @@
 // Two launches per step, so that the only cross-workgroup hand-off goes
 // through a kernel boundary (no device-wide fences or atomics):
 //
-//  step_kernel, one workgroup per (slice, KV group), slice-major, over a
-//  fixed number of slices S per group (the launch is the same for every step
-//  and can be captured in a graph); 8 waves for groups of up to 4 query
-//  heads, 4 for wider ones:
+//  step_kernel, one workgroup per (slice, KV group), over a fixed number of
+//  slices S per group (the launch is the same for every step and can be
+//  captured in a graph; ids slice-major, or chunk-major for wide groups
+//  split into chunks); 8 waves (4 for wide groups of fp32 d128 tiles):
 //   A. read the sequence length; for each of the group's G query heads rotate
 //      the query (float64 angles) and match the pre-RoPE query against the
-//      ring (two waves per head, each over half of its slots, or one wave per
-//      head for wide groups; 16 lanes per ring slot); derive the group's
-//      split-K plan and this workgroup's slice of keys.  The slice-0
-//      workgroup records every head's match result for the merge.
+//      ring (two waves per head, each over half of its slots, or up to two
+//      heads per wave for wide groups; 16 lanes per ring slot); derive the
+//      group's split-K plan and this workgroup's slice of keys.  The slice-0
+//      workgroup records every head's match result for the merge, and the
+//      last workgroup copies the hit heads' matched ring states for it.
 //   B. with a non-empty slice: split-K attention on the matrix cores, one
 //      partial state (o, m, l) per head.  Each wave's first tile under the
 //      plan a miss would give is loaded while the match runs, and kept when
@@ -29,9 +30,10 @@
 //      p_new one wave loads the tile a typical hit starts in instead.  With a
 //      fused append, the workgroup whose slice holds the new token stores it
 //      in the cache and patches it into the tile it loads.
-//  merge_kernel, one workgroup per query head: log-sum-exp merge of the
-//  reused state and the slices, the head's new ring entry and its output;
-//  with a fused append it also publishes the new length.
+//  merge_kernel, one workgroup per query head (one wave, or up to 16 for
+//  more than 32 slices): log-sum-exp merge of the reused state and the
+//  slices, the head's new ring entry and its output; with a fused append it
+//  also publishes the new length.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
