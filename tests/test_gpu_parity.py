@@ -54,6 +54,16 @@ SMALL = {
     "mqa_g64": ("8b_32k", dict(n_q_heads=64, n_kv_heads=1, context=1800, steps=16)),
     "g20": ("8b_32k", dict(n_q_heads=40, n_kv_heads=2, context=1200, steps=16)),
     "mqa_paged": ("paged_b8", dict(batch=2, n_kv_heads=1, ctx_range=(500, 1200), steps=12)),
+    # every remaining (dtype, d, paged, wide) instantiation of the step kernel
+    "f32_d128_wide": ("tiny", dict(head_dim=128, n_q_heads=16, n_kv_heads=2, context=1100, steps=16,
+                                   tau=0.5 * math.sqrt(128))),
+    "f32_d64_mqa": ("tiny", dict(n_q_heads=32, n_kv_heads=1, context=1300, steps=16)),
+    "f32_paged": ("paged_b8", dict(dtype="f32", batch=2, ctx_range=(400, 1100), steps=12)),
+    "f32_d64_paged_wide": ("paged_b8", dict(dtype="f32", head_dim=64, batch=2, n_q_heads=32,
+                                            n_kv_heads=4, ctx_range=(300, 900), steps=12,
+                                            tau=0.5 * math.sqrt(64))),
+    "d64_bf16_paged_wide": ("paged_b8", dict(head_dim=64, batch=2, n_q_heads=32, n_kv_heads=2,
+                                             ctx_range=(500, 1300), steps=12, tau=0.5 * math.sqrt(64))),
 }
 
 
@@ -117,7 +127,8 @@ def test_stale_cache_slots_do_not_leak(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_full", "8b_128k_p05", "paged_b8_small", "70b_small",
-                                  "ctx1", "mqa_g32", "mqa_paged"])
+                                  "ctx1", "mqa_g32", "mqa_paged", "f32_d128_wide",
+                                  "d64_bf16_paged_wide"])
 def test_fused_append_decode_every_step(name):
     base, kw = SMALL[name]
     w = workload(base, **kw)
