@@ -271,7 +271,7 @@ def test_seeded_ring_every_step(name):
 # HIP graph replay
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["8b_32k_ragged", "paged_b8_small"])
+@pytest.mark.parametrize("name", ["8b_32k_ragged", "paged_b8_small", "mqa_g32", "f32_d128_wide"])
 def test_graph_replays_equal_eager_steps(name):
     # one fused decode step is captured once and replayed for every token,
     # its input buffers refilled by eager copies between replays; every
