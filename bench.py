@@ -97,8 +97,15 @@ class Layer:
         import torch
         from kv_cache_reuse_amd import binding as B
         self.w, self.inp = w, inp
-        cfg = B.config_from_workload(w, max_context=max_context)
-        self.sess = B.MacSession(cfg)
+        if w.page_size:
+            # paged cache: the stream's page table (16-token pages from a
+            # shared, shuffled pool)
+            cfg = B.config_from_workload(w, n_pages=int(inp.n_pages),
+                                         max_pages_per_seq=int(inp.page_table.shape[1]))
+            self.sess = B.MacSession(cfg, page_table=inp.page_table)
+        else:
+            cfg = B.config_from_workload(w, max_context=max_context)
+            self.sess = B.MacSession(cfg)
         dev = torch.device("cuda")
         self.K = inp.k.to(dev)
         self.V = inp.v.to(dev)
@@ -129,7 +136,7 @@ class Layer:
         # append + match + split-K attention + merge: one library call
         B.mac_decode_step_append(s.ctx, self.q[t].data_ptr(), self.k_new[t].data_ptr(),
                                  self.v_new[t].data_ptr(), s.k_cache.data_ptr(),
-                                 s.v_cache.data_ptr(), 0, self.out[t].data_ptr(),
+                                 s.v_cache.data_ptr(), s._pt(), self.out[t].data_ptr(),
                                  self.match_n[t].data_ptr(), 0, st)
         self.t += 1
 
@@ -430,6 +437,29 @@ def mqa(steps, warmup, cache=None):
     return res
 
 
+def batch_point(steps, warmup, cache=None):
+    """A ragged batch on a paged cache: 8 sequences of 16K-64K keys (32 query
+    / 8 KV heads, d 128, bf16 K/V, 16-token pages), miss path.  Graph-replayed
+    steps, and the step kernel timed by HIP events in an eager run."""
+    from synth.streams import workload
+    w = workload("paged_b8", p_jump=1.0)
+    ms, recs, _, _ = run_point(w, 1.0, steps, warmup, 2, inputs_cache=cache)
+    st = summarize(w, ms, recs, steps)
+    _, recs_k, kms, kl = run_point(w, 1.0, steps, warmup, 2, kernel_timing=True,
+                                   inputs_cache=cache)
+    keys = sum(step_bytes(w, *r)[2] for r in recs_k)
+    kbytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(kl, 1)
+    kus = 1e3 * kms / max(kl, 1)
+    res = {"workload": "paged_b8: batch 8, contexts 16K-64K keys (ragged), 32 query / 8 KV heads, "
+                       "d 128, bf16 K/V, paged cache (16-token pages), miss path",
+           "us_per_step": st["us_per_step"], "eff_GBps": st["eff_GBps"],
+           "kernel_us": kus, "kernel_GBps": kbytes / kus / 1e3,
+           "kernel_pct_hbm_peak": 100.0 * kbytes / kus / 1e3 / HBM_PEAK_GBPS}
+    log(f"  batch: {res['us_per_step']:.1f} us/step, step kernel {kus:.1f} us "
+        f"({res['kernel_GBps']:.0f} GB/s of KV)")
+    return res
+
+
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
@@ -561,6 +591,7 @@ def main():
     ap.add_argument("--no-drift", action="store_true")
     ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--no-mqa", action="store_true")
+    ap.add_argument("--no-batch", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -671,6 +702,12 @@ def main():
         log("multi-layer graph: gen_16k shape, 32 layers")
         multi = multilayer()
 
+    # ---- a ragged batch on a paged cache
+    bt = None
+    if not args.no_batch:
+        log("batch: 8 ragged sequences (16K-64K keys), paged cache")
+        bt = batch_point(min(args.steps, 64), min(args.warmup, 8))
+
     # ---- MQA / groups wider than the 16-head tile
     mq = None
     if not args.no_mqa:
@@ -720,6 +757,7 @@ def main():
         "drift": drift,
         "multilayer": multi,
         "mqa": mq,
+        "batch": bt,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,
