@@ -439,8 +439,9 @@ def mqa(steps, warmup, cache=None):
 
 def batch_point(steps, warmup, cache=None):
     """A ragged batch on a paged cache: 8 sequences of 16K-64K keys (32 query
-    / 8 KV heads, d 128, bf16 K/V, 16-token pages), miss path.  Graph-replayed
-    steps, and the step kernel timed by HIP events in an eager run."""
+    / 8 KV heads, d 128, bf16 K/V, 16-token pages).  Miss path: graph-replayed
+    steps, and the step kernel timed by HIP events in an eager run; then the
+    graph-replayed step at jump probability 0.1 and 0."""
     from synth.streams import workload
     w = workload("paged_b8", p_jump=1.0)
     ms, recs, _, _ = run_point(w, 1.0, steps, warmup, 2, inputs_cache=cache)
@@ -457,6 +458,16 @@ def batch_point(steps, warmup, cache=None):
            "kernel_pct_hbm_peak": 100.0 * kbytes / kus / 1e3 / HBM_PEAK_GBPS}
     log(f"  batch: {res['us_per_step']:.1f} us/step, step kernel {kus:.1f} us "
         f"({res['kernel_GBps']:.0f} GB/s of KV)")
+    # the same batch at the stream's own jump rate and with no jumps
+    res["mixed"] = []
+    for p in (0.1, 0.0):
+        wp = workload("paged_b8", p_jump=p)
+        msp, rp, _, _ = run_point(wp, p, steps, warmup, 2, inputs_cache=cache)
+        sp = summarize(wp, msp, rp, steps)
+        res["mixed"].append({"p_jump": p, "us_per_step": sp["us_per_step"],
+                             "hit_rate": sp["hit_rate"], "group_all_hit": sp["group_all_hit"]})
+        log(f"  batch p={p}: {sp['us_per_step']:.1f} us/step (hit {sp['hit_rate']:.2f}, "
+            f"group all-hit {sp['group_all_hit']:.2f})")
     return res
 
 
@@ -706,7 +717,7 @@ def main():
     bt = None
     if not args.no_batch:
         log("batch: 8 ragged sequences (16K-64K keys), paged cache")
-        bt = batch_point(min(args.steps, 64), min(args.warmup, 8))
+        bt = batch_point(min(args.steps, 64), min(args.warmup, 8), {})
 
     # ---- MQA / groups wider than the 16-head tile
     mq = None

@@ -38,7 +38,8 @@ mac_status ok() {
 // Split-K workgroups a miss step aims for: one workgroup per compute unit
 // of a 256-CU part.
 constexpr int kTargetWorkgroups = 256;
-// Keys per slice a full-length sequence aims for (the default slice count)
+// Keys per slice of a full-length sequence above which the default slice
+// count takes a second round of workgroups
 constexpr int64_t kSliceTarget = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -125,15 +126,18 @@ Layout layout(const mac_config* c) {
   const int groups = c->batch * c->n_kv_heads * n_chunks(c);   // matched groups
   int S = c->max_slices;
   if (S == 0) {
-    // enough slices to give every compute unit a workgroup; then whole
-    // multiples of that, so that a full-length sequence's slices hold about
-    // kSliceTarget keys: longer slices left a batch's longest sequences (or
-    // the slowest XCDs) running alone at the end, and the hardware deals
-    // the extra rounds of workgroups to whichever units are free
+    // enough slices to give every compute unit a workgroup, and a second
+    // round of as many when a full-length sequence's slices would otherwise
+    // hold more than about 1.5 kSliceTarget keys.  With one round, a batch
+    // step in which a few sequences miss waits for their few workgroups to
+    // stream a quarter of a sequence each; the hardware deals the second
+    // round to whichever units are free.  More rounds cost the hit path a
+    // repeated match per round (every workgroup matches before it knows
+    // whether its slice is empty).
     const int base = mac::ceil_div(kTargetWorkgroups, groups);
     const int64_t per_round = (int64_t)base * kSliceTarget;
-    const int rounds = (int)((L.capacity + per_round / 2) / per_round);
-    S = base * (rounds > 1 ? rounds : 1);
+    const int rounds = L.capacity * 2 > per_round * 3 ? 2 : 1;
+    S = base * rounds;
     // never more slices than the longest context can fill
     const int cap = (int)((L.capacity + mac::kSliceMin - 1) / mac::kSliceMin) + 1;
     if (S > cap) S = cap;
