@@ -49,8 +49,9 @@ struct Layout {
   // ring
   size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
   // workspace
-  size_t w_po, w_pml, w_heads, w_reuse, w_invf, w_out, w_save, ws_bytes;
+  size_t w_po, w_pml, w_heads, w_reuse, w_pub, w_invf, w_out, w_save, ws_bytes;
   int slices;
+  int first;            // slices per group in the first round of workgroups
   int64_t capacity;     // keys per sequence
   int tiles_per_seq;    // contiguous cache
 };
@@ -125,6 +126,7 @@ Layout layout(const mac_config* c) {
   L.tiles_per_seq = c->page_size ? 0 : mac::ceil_div(c->max_context, mac::kTile);
   const int groups = c->batch * c->n_kv_heads * n_chunks(c);   // matched groups
   int S = c->max_slices;
+  L.first = 0;
   if (S == 0) {
     // enough slices to give every compute unit a workgroup, and a second
     // round of as many when a full-length sequence's slices would otherwise
@@ -138,6 +140,7 @@ Layout layout(const mac_config* c) {
     const int64_t per_round = (int64_t)base * kSliceTarget;
     const int rounds = L.capacity * 2 > per_round * 3 ? 2 : 1;
     S = base * rounds;
+    L.first = base;
     // never more slices than the longest context can fill
     const int cap = (int)((L.capacity + mac::kSliceMin - 1) / mac::kSliceMin) + 1;
     if (S > cap) S = cap;
@@ -147,6 +150,7 @@ Layout layout(const mac_config* c) {
   const size_t G = chunk_heads(c);
   if (S * G > (size_t)mac::kMergeCap) S = mac::kMergeCap / (int)G;
   L.slices = S;
+  if (L.first <= 0 || L.first > S) L.first = S;
   off = 0;
   L.w_po = off;      off = align256(off + (size_t)groups * S * G * d * 4);
   L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
@@ -155,6 +159,7 @@ Layout layout(const mac_config* c) {
   L.w_invf = off;  off = align256(off + (d / 2) * 8);
   L.w_out = off;   off = align256(off + bh * d * 4);          // ring seeding: discarded outputs
   L.w_save = off;  off = align256(off + (size_t)c->batch * 4); // ring seeding: saved lengths
+  L.w_pub = off;   off = align256(off + (size_t)groups * 8);    // second round: published plans
   L.ws_bytes = off;
   return L;
 }
@@ -276,6 +281,9 @@ mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t*
   hipError_t e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
                                       cfg->batch * cfg->n_q_heads, 0,
                                       static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)   // no published plan yet (all ones never matches a ring count)
+    e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws + L.w_pub),
+                             (int)((L.ws_bytes - L.w_pub) / 4), -1, static_cast<hipStream_t>(stream));
   if (e == hipSuccess)
     e = mac::launch_inv_freq(reinterpret_cast<double*>(ctx->ws + L.w_invf), cfg->head_dim,
                              cfg->rope_theta, static_cast<hipStream_t>(stream));
@@ -372,6 +380,8 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.dist_out = nullptr;
   a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
   a.reuse_o = reinterpret_cast<float*>(ctx->ws + L.w_reuse);
+  a.plan_pub = reinterpret_cast<unsigned long long*>(ctx->ws + L.w_pub);
+  a.part.first = L.first;
   a.reuse_ml = a.reuse_o + (size_t)c.batch * c.n_q_heads * c.head_dim;
   a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
   a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);

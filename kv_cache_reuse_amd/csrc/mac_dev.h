@@ -167,13 +167,21 @@ struct Plan {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-__host__ __device__ __forceinline__ Plan make_plan(int lo, int n, int band, int max_slices) {
+// first: slices per group in the first round of workgroups (max_slices when
+// the launch fills the GPU in one round).  With a second round, the slices
+// after p_new are capped at first - 2: every slice a hit needs (those and the
+// first one before p_new) is then in the first round, and so is one slice a
+// hit leaves empty (slice first - 1, which copies the reused states).
+__host__ __device__ __forceinline__ Plan make_plan(int lo, int n, int band, int max_slices,
+                                                   int first) {
   Plan p;
   p.hi = n;
   p.mid = n - band > 0 ? n - band : 0;
   p.lo = lo < p.mid ? lo : p.mid;
   const int lpre = p.mid - p.lo, lpost = p.hi - p.mid;
-  const int post_cap = max_slices / 2 > 1 ? max_slices / 2 : 1;
+  int post_cap = max_slices / 2;
+  if (first < max_slices && post_cap > first - 2) post_cap = first - 2;
+  if (post_cap < 1) post_cap = 1;
   p.n_post = lpost > 0 ? min(ceil_div(lpost, kSliceMin), post_cap) : 0;
   const int pre_cap = max_slices - p.n_post;
   p.n_pre = lpre > 0 ? min(ceil_div(lpre, kSliceMin), pre_cap) : 0;
@@ -247,6 +255,7 @@ struct PartialView {
   float* o;    // [groups][S][G][D]
   float* ml;   // [groups][S][G][2]
   int S;
+  int first;   // slices per group in the first round of workgroups (S: one round)
 };
 
 struct StepArgs {
@@ -273,6 +282,10 @@ struct StepArgs {
   int batch, hq, hkv, group, band, nchunk;
   float tau2;               // tau^2 rounded to fp32
   double theta;
+  // (last, so that the fields the match reads first keep their offsets)
+  // [groups] (ring count of the group's first head << 32 | plan start),
+  // published by each group's slice-0 workgroup once its match is done
+  unsigned long long* plan_pub;
 };
 
 }  // namespace mac

@@ -120,6 +120,7 @@ struct Shared {
   float o[NE][OC][D + 1];
   // fused append: the new token's key and value
   __attribute__((aligned(16))) unsigned char patch[2 * D * 4];
+  int leave;   // second round: the workgroup's slice is empty
 };
 
 // =========================================================== phase A ====
@@ -364,7 +365,11 @@ __host__ __device__ constexpr int step_waves() {
 // waves) over all their slots; a separate instantiation so that the narrow
 // case's code has no conditional loads (which make the compiler wait for
 // every load in flight).  In both, four waves stream the tiles.
-template <typename T, int D, bool PAGED, bool WIDE>
+// R2: a narrow launch with a second round of workgroups (more slices per
+// group than one round fills): the slice-0 workgroup publishes its plan
+// start and second-round workgroups whose slice is empty leave early.  A
+// separate instantiation, so that one-round launches carry none of it.
+template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false>
 __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
   constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
   constexpr int NWB = 4;                        // waves that stream tiles
@@ -430,10 +435,33 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   const bool append = fused && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
   const int p_new = n - a.band > 0 ? n - a.band : 0;
+  // A second-round workgroup (two rounds per launch) whose slice this step's
+  // plan leaves empty leaves before its tile loads and its match, when the
+  // group's slice-0 workgroup has already published the plan start (tagged
+  // with the ring count of the group's first head, so an earlier step's
+  // value never matches).  Wave 0 decides for the whole workgroup.
+  if (R2 && slice >= a.part.first) {
+    // (a plain load: an atomic one would keep the compiler from reading the
+    // page table through scalar loads in the tile loop; a stale value only
+    // fails the tag check, and the workgroup then matches as usual)
+    const unsigned long long pub = a.plan_pub[grp];
+    const int cnt0 = a.ring.count[b * a.hq + kvh * G];
+    // every lane decides (so every wave consumes the load); wave 0's
+    // decision is the workgroup's
+    int leave = 0;
+    if (static_cast<unsigned>(pub >> 32) == static_cast<unsigned>(cnt0)) {
+      const Plan pp = make_plan(static_cast<int>(static_cast<unsigned>(pub)), n, a.band, a.part.S,
+                                a.part.first);
+      leave = slice >= pp.n_pre + pp.n_post;
+    }
+    if (wave == 0 && lane == 0) sh.leave = leave;
+    __syncthreads();
+    if (sh.leave) return;
+  }
   // The group's plan when any of its heads misses does not depend on the
   // match: this wave's first tile under it is loaded while the match runs
   // and kept if the real plan gives the wave the same first tile.
-  const Plan ps = make_plan(0, n, a.band, a.part.S);
+  const Plan ps = make_plan(0, n, a.band, a.part.S, a.part.first);
   int ska = 0, ske = 0;
   if (slice < ps.n_pre + ps.n_post) slice_range(ps, slice, &ska, &ske);
   const int st0 = ska / kTile, st1 = (ske + kTile - 1) / kTile;
@@ -521,7 +549,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     lo = min(lo, sh.head[i].s);
     smax = max(smax, sh.head[i].s);
   }
-  const Plan p = make_plan(lo, n, a.band, a.part.S);
+  const Plan p = make_plan(lo, n, a.band, a.part.S, a.part.first);
   const int nact = p.n_pre + p.n_post;
 
   // ---------------------------------------------------------------- B ----
@@ -748,6 +776,16 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
       }
       if (i < nt) process(tw + NWB * i, kA, vA);
     }
+    // slice 0 publishes the plan start for the second round of workgroups.
+    // The store comes after the tile loop in program order (a global store
+    // ahead of the loop would keep the compiler from reading the page table
+    // through scalar loads there), but a wave that streams no tiles reaches
+    // it right after the plan.
+    if (R2 && slice == 0 && wave == NWB && lane == 0)
+      __hip_atomic_store(a.plan_pub + grp,
+                         (static_cast<unsigned long long>(static_cast<unsigned>(sh.head[0].cnt)) << 32) |
+                             static_cast<unsigned>(lo),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lsum += shfl_xor_f(lsum, 16);
     lsum += shfl_xor_f(lsum, 32);
 
@@ -813,9 +851,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   }
   // the hit heads' matched ring states, copied to rows of their own so that
   // the merge kernel loads them in its first round instead of behind the
-  // records.  The group's last workgroup does it: on a hit its slice is
-  // usually empty, and when every head misses there is nothing to copy.
-  if (slice == a.part.S - 1) {
+  // records.  The last workgroup of the first round does it: on a hit its
+  // slice is empty, and when every head misses there is nothing to copy.
+  if (slice == a.part.first - 1) {
     for (int idx = tid; idx < G * D; idx += NTH) {
       const int hh = idx / D, dim = idx % D;
       if (sh.head[hh].hit) {
@@ -907,7 +945,7 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   int lo = hs.s;
   for (int i = 0; i < G; ++i) lo = min(lo, hsg[i].s);
   const int n = hs.n;
-  const Plan p = make_plan(lo, n, a.band, S);
+  const Plan p = make_plan(lo, n, a.band, S, a.part.first);
   const int npart = p.n_pre + p.n_post;
   const int ke = k1 < npart ? k1 : npart;               // this wave's live slices: [k0, ke)
   if (MW && wave != 0 && k0 < ke) load_o(k0);
@@ -1067,13 +1105,18 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   if (ev0) (void)hipEventRecord(ev0, st);
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
+  const bool r2 = !wide && a.part.first < a.part.S;   // narrow, two rounds
 #define L_STEP(T, D)                                                                              \
   if (paged && wide)                                                                                 \
     hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+  else if (paged && r2)                                                                              \
+    hipLaunchKernelGGL((step_kernel<T, D, true, false, true>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else if (paged)                                                                                    \
     hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else if (wide)                                                                                     \
     hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+  else if (r2)                                                                                       \
+    hipLaunchKernelGGL((step_kernel<T, D, false, false, true>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
   MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP

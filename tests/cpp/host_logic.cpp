@@ -53,11 +53,15 @@ void check_tiles(int D) {
     }
 }
 
-void check_plan(int lo, int n, int band, int S) {
-  mac::Plan p = mac::make_plan(lo, n, band, S);
+void check_plan(int lo, int n, int band, int S, int first) {
+  mac::Plan p = mac::make_plan(lo, n, band, S, first);
   const int mid = n - band > 0 ? n - band : 0;
   CHECK(p.mid == mid && p.hi == n, "mid/hi");
   CHECK(p.n_pre + p.n_post <= S, "too many slices %d + %d > %d", p.n_pre, p.n_post, S);
+  // with a second round, what a hit needs (the slices after p_new and the
+  // first one before it) stays below first - 1, the workgroup that copies
+  // the reused states
+  if (first < S) CHECK(p.n_post <= (first - 2 > 1 ? first - 2 : 1), "%d slices after p_new, first %d", p.n_post, first);
   CHECK((p.lo < p.mid) == (p.n_pre > 0), "pre slices %d for [%d, %d)", p.n_pre, p.lo, p.mid);
   CHECK((p.mid < p.hi) == (p.n_post > 0), "post slices %d for [%d, %d)", p.n_post, p.mid, p.hi);
   // walk the slices in key order: pre slices (indices n_post ..), then post
@@ -131,15 +135,18 @@ int main() {
     int mid = n - band > 0 ? n - band : 0;
     int lo = rng() % 2 ? 0 : (int)(rng() % (mid + 1));
     int S = Ss[rng() % 7];
-    check_plan(lo, n, band, S);
+    // one round, or a first round of about half the slices
+    int first = rng() % 2 ? S : (S / 2 > 0 ? S / 2 : 1);
+    check_plan(lo, n, band, S, first);
   }
   for (int groups : {1, 2, 3, 8, 16, 64})
     for (int S : {2, 5, 32, 128, 1024}) check_coords(groups, 1, S);
   for (int real : {1, 2, 3, 8})
     for (int nc : {2, 3, 4})
       for (int S : {2, 5, 13, 64, 128}) check_coords(real * nc, nc, S);
-  check_plan(0, 131072 + 512, 256, 128);
-  check_plan(131072 + 300 - 256 - 1, 131072 + 300, 256, 128);
+  check_plan(0, 131072 + 512, 256, 128, 128);
+  check_plan(131072 + 300 - 256 - 1, 131072 + 300, 256, 128, 128);
+  check_plan(131072 + 300 - 256 - 1, 131072 + 300, 256, 8, 4);
   if (fails) {
     std::printf("%d failures\n", fails);
     return 1;
