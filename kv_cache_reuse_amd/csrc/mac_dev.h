@@ -225,7 +225,8 @@ __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* 
 // into nchunk chunks read the same keys in every chunk: their ids run
 // chunk-major, each chunk's run padded to a multiple of 8, so the chunks of
 // a slice share an XCD and its L2 reads of the slice's tiles.  Padding ids
-// return false.
+// return false, with slice = S (a slice no plan gives work) and a valid
+// group.
 constexpr int kXcds = 8;
 
 __host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S) {
@@ -244,10 +245,9 @@ __host__ __device__ __forceinline__ bool step_coords(int id, int groups, int nch
   const int nreal = groups / nchunk;
   const int per = nreal * S, run = (per + kXcds - 1) / kXcds * kXcds;
   const int c = id / run, j = id % run;
-  if (j >= per) return false;
   *grp = (j % nreal) * nchunk + c;
-  *slice = j / nreal;
-  return true;
+  *slice = j < per ? j / nreal : S;
+  return j < per;
 }
 
 // Partial states: o unnormalized, m in log2 units of the scaled score.

@@ -382,9 +382,11 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
   __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
+  // (padding ids of a chunked group get slice S: no plan gives it work, and
+  // it writes nothing; no early return here, so that the compiler issues the
+  // argument loads phase A needs together with the ones for this mapping)
   int grp, slice;
-  // (padding ids of a chunked group leave before any barrier)
-  if (!step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice)) return;
+  step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice);
   const int b = grp / a.hkv, kvh = grp % a.hkv;
   const int kvr = kvh / a.nchunk;          // the KV head whose cache is read
   const int G = a.group;

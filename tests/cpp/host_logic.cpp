@@ -101,6 +101,7 @@ void check_coords(int groups, int nchunk, int S) {
   for (int id = 0; id < grid; ++id) {
     int g = -1, s = -1;
     if (!mac::step_coords(id, groups, nchunk, S, &g, &s)) {
+      CHECK(s == S && g >= 0 && g < groups, "padding id %d -> (%d, %d)", id, g, s);
       ++pad;
       continue;
     }
