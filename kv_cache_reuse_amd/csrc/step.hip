@@ -761,7 +761,10 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     // prefetches included, before the current tile's math.
     // nt tiles for this wave: t0 + wave, + NWB, ...; pairs in a loop with one
     // exit (a loop left in the middle makes the compiler wait for every
-    // load in flight at its header), then the odd one
+    // load in flight at its header) while the tile it prefetches is one the
+    // wave processes, then the last one or two tiles with no prefetch (a
+    // tile loaded and never used would still hold the wave until it
+    // arrived)
     const int tlast = t1 - 1;
     const int tw = t0 + wave;
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
@@ -769,14 +772,21 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile(tw, kA, vA);
       int i = 0;
-      for (; i + 1 < nt; i += 2) {
+      for (; i + 2 < nt; i += 2) {
         const int t = tw + NWB * i;
         load_tile(t + NWB, kB, vB);
         process(t, kA, vA);
         load_tile(min(t + 2 * NWB, tlast), kA, vA);
         process(t + NWB, kB, vB);
       }
-      if (i < nt) process(tw + NWB * i, kA, vA);
+      if (i + 1 < nt) {
+        const int t = tw + NWB * i;
+        load_tile(t + NWB, kB, vB);
+        process(t, kA, vA);
+        process(t + NWB, kB, vB);
+      } else {
+        process(tw + NWB * i, kA, vA);
+      }
     }
     // slice 0 publishes the plan start for the second round of workgroups.
     // The store comes after the tile loop in program order (a global store
