@@ -227,7 +227,17 @@ __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* 
 // a slice share an XCD and its L2 reads of the slice's tiles.  Padding ids
 // return false, with slice = S (a slice no plan gives work) and a valid
 // group.
+//
+// A narrow launch with a second round of workgroups (slices >= first, dealt
+// to compute units as they come free) can take an order of the sequences,
+// longest first: its second-round ids then run sequence by sequence in that
+// order (slice-major within a sequence), so each XCD's queue holds its
+// longest slices first and the units that finish short first-round slices
+// take them (longest-processing-time-first list scheduling).  Any
+// permutation gives the same bijection, so a stale order costs time, never
+// results.
 constexpr int kXcds = 8;
+constexpr int kOrderMax = 64;   // sequences an order can hold
 
 __host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S) {
   if (nchunk == 1) return groups * S;
@@ -236,8 +246,17 @@ __host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S)
 }
 
 __host__ __device__ __forceinline__ bool step_coords(int id, int groups, int nchunk, int S,
-                                                     int* grp, int* slice) {
+                                                     int* grp, int* slice, int hkv = 1, int first = 0,
+                                                     const unsigned* order = nullptr) {
   if (nchunk == 1) {
+    const int r1 = groups * first;
+    if (order && id >= r1) {
+      const int per = hkv * (S - first), j = id - r1;
+      const int rem = j % per, k = j / per;   // order byte k, four to a word
+      *grp = static_cast<int>((order[k >> 2] >> (8 * (k & 3))) & 0xffu) * hkv + rem % hkv;
+      *slice = first + rem / hkv;
+      return true;
+    }
     *grp = id % groups;
     *slice = id / groups;
     return true;
@@ -286,6 +305,10 @@ struct StepArgs {
   // [groups] (ring count of the group's first head << 32 | plan start),
   // published by each group's slice-0 workgroup once its match is done
   unsigned long long* plan_pub;
+  // sequences longest first, for the second round's ids (used when
+  // batch <= kOrderMax), one byte each, little-endian in 32-bit words;
+  // read only by second-round workgroups
+  unsigned order[kOrderMax / 4];
 };
 
 }  // namespace mac

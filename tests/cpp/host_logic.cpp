@@ -4,6 +4,7 @@
 // straddle p_new, with every slice non-empty and at most max_slices of them.
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <random>
 #include <vector>
 
@@ -93,14 +94,36 @@ void check_plan(int lo, int n, int band, int S, int first) {
 
 // Every (group, slice) of the step launch gets exactly one workgroup id;
 // padding ids are the only ones left over; the chunks of a wide group's
-// slice share an XCD (ids congruent mod 8).
-void check_coords(int groups, int nchunk, int S) {
+// slice share an XCD (ids congruent mod 8).  With a sequence order (narrow
+// launches, hkv heads per sequence, `first` slices in the first round), the
+// first round keeps the slice-major ids and the second round's ids visit
+// the sequences in the order given.
+void check_coords(int groups, int nchunk, int S, int hkv = 1, int first = 0,
+                  const std::vector<unsigned char>* ord = nullptr) {
   const int grid = mac::step_grid(groups, nchunk, S);
   std::vector<int> seen((size_t)groups * S, 0), xcd((size_t)groups * S, -1);
-  int pad = 0;
+  std::vector<unsigned> words;
+  if (ord) {
+    words.assign((ord->size() + 3) / 4, 0u);
+    for (size_t k = 0; k < ord->size(); ++k) words[k / 4] |= (unsigned)(*ord)[k] << (8 * (k % 4));
+  }
+  int pad = 0, prev_rank = 0;
   for (int id = 0; id < grid; ++id) {
     int g = -1, s = -1;
-    if (!mac::step_coords(id, groups, nchunk, S, &g, &s)) {
+    const bool real = mac::step_coords(id, groups, nchunk, S, &g, &s, hkv, first,
+                                       ord ? words.data() : nullptr);
+    if (ord && real) {
+      if (id < groups * first) {
+        CHECK(g == id % groups && s == id / groups, "first-round id %d -> (%d, %d)", id, g, s);
+      } else {
+        CHECK(s >= first, "second-round id %d -> slice %d < first %d", id, s, first);
+        int rank = 0;
+        while (rank < (int)ord->size() && (*ord)[rank] != g / hkv) ++rank;
+        CHECK(rank >= prev_rank, "id %d: sequence rank %d after rank %d", id, rank, prev_rank);
+        prev_rank = rank;
+      }
+    }
+    if (!real) {
       CHECK(s == S && g >= 0 && g < groups, "padding id %d -> (%d, %d)", id, g, s);
       ++pad;
       continue;
@@ -142,6 +165,17 @@ int main() {
   }
   for (int groups : {1, 2, 3, 8, 16, 64})
     for (int S : {2, 5, 32, 128, 1024}) check_coords(groups, 1, S);
+  // second-round orders: batch x hkv groups, first < S, random permutations
+  std::mt19937 orng(7);
+  for (int batch : {2, 3, 8, 17, 64})
+    for (int hkv : {1, 2, 8})
+      for (int S : {2, 5, 8, 16}) {
+        std::vector<unsigned char> ord(batch);
+        for (int b = 0; b < batch; ++b) ord[b] = (unsigned char)b;
+        std::shuffle(ord.begin(), ord.end(), orng);
+        for (int first = 1; first < S; first += (S > 4 ? 3 : 1))
+          check_coords(batch * hkv, 1, S, hkv, first, &ord);
+      }
   for (int real : {1, 2, 3, 8})
     for (int nc : {2, 3, 4})
       for (int S : {2, 5, 13, 64, 128}) check_coords(real * nc, nc, S);

@@ -46,6 +46,10 @@ def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] 
     paged = bool(w.page_size) if paged is None else paged
     if paged:
         table = inp.page_table
+        if capacity:   # more table columns, never read: positions past every context
+            pages = -(-capacity // 16)
+            if pages > table.shape[1]:
+                table = np.pad(table, ((0, 0), (0, pages - table.shape[1])))
         cfg = B.config_from_workload(w.replace(page_size=16), n_pages=int(inp.n_pages),
                                      max_pages_per_seq=int(table.shape[1]),
                                      max_slices=max_slices)
