@@ -396,18 +396,18 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.group = chunk_heads(&c);
   a.band = c.band;
   a.tau2 = static_cast<float>((double)c.tau * (double)c.tau);
-  a.theta = c.rope_theta;
   // the second round's sequence order, longest first by the host mirror
   // (ties by index); the mirror is exact for calls made eagerly, and a
   // graph replays the order it captured, which stays right while every
   // sequence grows by one key per step
-  const int nb = c.batch < mac::kOrderMax ? c.batch : mac::kOrderMax;
-  unsigned char ord[mac::kOrderMax] = {};
-  for (int b = 0; b < nb; ++b) ord[b] = static_cast<unsigned char>(b);
-  std::stable_sort(ord, ord + nb,
-                   [ctx](unsigned char x, unsigned char y) { return ctx->mirror[x] > ctx->mirror[y]; });
-  for (int k = 0; k < mac::kOrderMax / 4; ++k)
-    a.order[k] = ord[4 * k] | ord[4 * k + 1] << 8 | ord[4 * k + 2] << 16 | (unsigned)ord[4 * k + 3] << 24;
+  a.order = 0;
+  if (c.batch > 1 && c.batch <= mac::kOrderMax) {
+    unsigned char ord[mac::kOrderMax];
+    for (int b = 0; b < c.batch; ++b) ord[b] = static_cast<unsigned char>(b);
+    std::stable_sort(ord, ord + c.batch,
+                     [ctx](unsigned char x, unsigned char y) { return ctx->mirror[x] > ctx->mirror[y]; });
+    for (int k = 0; k < c.batch; ++k) a.order |= static_cast<unsigned long long>(ord[k]) << (4 * k);
+  }
   return a;
 }
 

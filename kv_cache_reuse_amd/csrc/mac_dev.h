@@ -237,7 +237,7 @@ __host__ __device__ __forceinline__ void slice_range(const Plan& p, int i, int* 
 // permutation gives the same bijection, so a stale order costs time, never
 // results.
 constexpr int kXcds = 8;
-constexpr int kOrderMax = 64;   // sequences an order can hold
+constexpr int kOrderMax = 16;   // sequences an order can hold (4 bits each)
 
 __host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S) {
   if (nchunk == 1) return groups * S;
@@ -247,13 +247,13 @@ __host__ __device__ __forceinline__ int step_grid(int groups, int nchunk, int S)
 
 __host__ __device__ __forceinline__ bool step_coords(int id, int groups, int nchunk, int S,
                                                      int* grp, int* slice, int hkv = 1, int first = 0,
-                                                     const unsigned* order = nullptr) {
+                                                     bool ordered = false, unsigned long long order = 0) {
   if (nchunk == 1) {
     const int r1 = groups * first;
-    if (order && id >= r1) {
+    if (ordered && id >= r1) {
       const int per = hkv * (S - first), j = id - r1;
-      const int rem = j % per, k = j / per;   // order byte k, four to a word
-      *grp = static_cast<int>((order[k >> 2] >> (8 * (k & 3))) & 0xffu) * hkv + rem % hkv;
+      const int rem = j % per, k = j / per;   // the sequence in nibble k
+      *grp = static_cast<int>((order >> (4 * k)) & 15u) * hkv + rem % hkv;
       *slice = first + rem / hkv;
       return true;
     }
@@ -300,15 +300,15 @@ struct StepArgs {
   // addressing uses the real head, virtual index / nchunk.
   int batch, hq, hkv, group, band, nchunk;
   float tau2;               // tau^2 rounded to fp32
-  double theta;
+  // sequences longest first, for the second round's ids (used when
+  // 1 < batch <= kOrderMax): nibble k holds the sequence of rank k.  (This
+  // keeps the argument block at 256 bytes; a larger block cost the hit
+  // path time even when no workgroup read the extra bytes.)
+  unsigned long long order;
   // (last, so that the fields the match reads first keep their offsets)
   // [groups] (ring count of the group's first head << 32 | plan start),
   // published by each group's slice-0 workgroup once its match is done
   unsigned long long* plan_pub;
-  // sequences longest first, for the second round's ids (used when
-  // batch <= kOrderMax), one byte each, little-endian in 32-bit words;
-  // read only by second-round workgroups
-  unsigned order[kOrderMax / 4];
 };
 
 }  // namespace mac

@@ -369,14 +369,6 @@ __host__ __device__ constexpr int step_waves() {
 // group than one round fills): the slice-0 workgroup publishes its plan
 // start and second-round workgroups whose slice is empty leave early.  A
 // separate instantiation, so that one-round launches carry none of it.
-// The sequence order in the step kernel's argument block, read in place
-// (indexing the by-value argument makes the compiler copy all of it to
-// scratch memory)
-__device__ __forceinline__ const unsigned* kernarg_order() {
-  const char* base = (const char*)__builtin_amdgcn_kernarg_segment_ptr();   // constant -> generic
-  return reinterpret_cast<const unsigned*>(base + offsetof(StepArgs, order));
-}
-
 template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false>
 __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
   constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
@@ -395,7 +387,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   // argument loads phase A needs together with the ones for this mapping)
   int grp, slice;
   step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice, a.hkv, a.part.first,
-              a.batch > 1 && a.batch <= kOrderMax ? kernarg_order() : nullptr);
+              R2 && a.batch > 1 && a.batch <= kOrderMax, a.order);
   const int b = grp / a.hkv, kvh = grp % a.hkv;
   const int kvr = kvh / a.nchunk;          // the KV head whose cache is read
   const int G = a.group;
