@@ -39,9 +39,10 @@ mac_status ok() {
 // Split-K workgroups a miss step aims for: one workgroup per compute unit
 // of a 256-CU part.
 constexpr int kTargetWorkgroups = 256;
-// Keys per slice of a full-length sequence above which the default slice
-// count takes a second round of workgroups
+// Keys per slice of a full-length sequence that the default slice count
+// aims for, by adding rounds of workgroups (at most kMaxRounds)
 constexpr int64_t kSliceTarget = 4096;
+constexpr int kMaxRounds = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -129,17 +130,22 @@ Layout layout(const mac_config* c) {
   int S = c->max_slices;
   L.first = 0;
   if (S == 0) {
-    // enough slices to give every compute unit a workgroup, and a second
-    // round of as many when a full-length sequence's slices would otherwise
-    // hold more than about 1.5 kSliceTarget keys.  With one round, a batch
-    // step in which a few sequences miss waits for their few workgroups to
-    // stream a quarter of a sequence each; the hardware deals the second
-    // round to whichever units are free.  More rounds cost the hit path a
-    // repeated match per round (every workgroup matches before it knows
-    // whether its slice is empty).
+    // enough slices to give every compute unit a workgroup, and further
+    // rounds of as many when a full-length sequence's slices would otherwise
+    // hold more than about 1.5 kSliceTarget keys: one round per kSliceTarget
+    // keys a slice of the first round would hold, up to kMaxRounds.  With
+    // one round, a batch step in which a few sequences miss waits for their
+    // few workgroups to stream a quarter of a sequence each; the hardware
+    // deals the later rounds to whichever units are free.  Each later round
+    // costs a hit step about 1 us: its workgroups leave as soon as they read
+    // the group's published plan start.
     const int base = mac::ceil_div(kTargetWorkgroups, groups);
     const int64_t per_round = (int64_t)base * kSliceTarget;
-    const int rounds = L.capacity * 2 > per_round * 3 ? 2 : 1;
+    int rounds = 1;
+    if (L.capacity * 2 > per_round * 3) {
+      const int64_t r = (L.capacity + per_round - 1) / per_round;
+      rounds = r < kMaxRounds ? (int)r : kMaxRounds;
+    }
     S = base * rounds;
     L.first = base;
     // never more slices than the longest context can fill

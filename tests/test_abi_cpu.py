@@ -80,6 +80,25 @@ def test_sizes_of_a_valid_config(B):
     assert B.mac_kv_cache_bytes(paged) == 1000 * 8 * 16 * 128 * 2
 
 
+@pytest.mark.parametrize("name,capacity,slices", [
+    ("8b_128k", 131200, 32),      # 8 groups: one round of 32 slices per group
+    ("paged_b8", 20000, 4),       # 64 groups: one round of 4
+    ("paged_b8", 30000, 8),       # two rounds
+    ("paged_b8", 50000, 16),      # ceil(50000 / 16384) = 4 rounds
+    ("paged_b8", 70000, 16),      # capped at 4 rounds
+])
+def test_default_slice_count(B, name, capacity, slices):
+    # the workspace holds the split-K partial states of every slice, so the
+    # default slice count shows as the size of an explicit one
+    from synth.streams import workload
+    w = workload(name).replace(page_size=0)
+    default = B.mac_workspace_bytes(B.config_from_workload(w, max_context=capacity))
+    assert default == B.mac_workspace_bytes(B.config_from_workload(w, max_context=capacity,
+                                                                   max_slices=slices))
+    assert default != B.mac_workspace_bytes(B.config_from_workload(w, max_context=capacity,
+                                                                   max_slices=slices + 1))
+
+
 def test_pointer_and_capacity_errors_come_before_device_calls(B):
     lib = B.library()
     cfg = valid_cfg(B)

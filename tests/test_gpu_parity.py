@@ -93,20 +93,23 @@ def test_merge_over_many_slices(max_slices):
     assert_report(rep, f"slices{max_slices}")
 
 
-@pytest.mark.parametrize("fused,page_size", [(False, 0), (True, 0), (False, 16), (True, 16)])
-def test_two_rounds_every_step(fused, page_size):
-    # a capacity far above the contexts gives the default launch a second
-    # round of workgroups (8 slices per group, 4 in the first round): the
-    # slice-0 workgroups publish their plan start and second-round
-    # workgroups with an empty slice leave early on hit steps.  The ragged
-    # contexts give the second round's ids a sequence order (longest first)
-    # other than the batch order.
+@pytest.mark.parametrize("fused,page_size,capacity", [(False, 0, 30000), (True, 0, 30000),
+                                                       (False, 16, 30000), (True, 16, 30000),
+                                                       (True, 0, 70000), (False, 16, 70000)])
+def test_two_rounds_every_step(fused, page_size, capacity):
+    # a capacity far above the contexts gives the default launch more
+    # rounds of workgroups (4 slices per group in the first round; 8 slices
+    # in all at capacity 30000, 16 at 70000): the slice-0 workgroups publish
+    # their plan start and later-round workgroups with an empty slice leave
+    # early on hit steps.  The ragged contexts give the later rounds' ids a
+    # sequence order (longest first) other than the batch order.
     w = workload("paged_b8", page_size=page_size, ctx_range=(700, 2300), steps=24, p_jump=0.1)
-    say(f"[two_rounds fused={fused} page_size={page_size}] {w}")
+    say(f"[rounds fused={fused} page_size={page_size} capacity={capacity}] {w}")
     inp = make_inputs(w)
-    gpu = run_gpu(w, inp, capacity=30000, fused=fused)
+    gpu = run_gpu(w, inp, capacity=capacity, fused=fused)
+    assert gpu.session.cfg.max_slices == 0
     rep = check_groups(w, inp, gpu, all_groups(w))
-    assert_report(rep, f"two_rounds:{fused}:{page_size}")
+    assert_report(rep, f"rounds:{fused}:{page_size}:{capacity}")
 
 
 @pytest.mark.parametrize("name,period", [("8b_32k", 3), ("70b_128k", 3), ("tiny", 2)])
