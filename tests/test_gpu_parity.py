@@ -112,6 +112,20 @@ def test_two_rounds_every_step(fused, page_size, capacity):
     assert_report(rep, f"rounds:{fused}:{page_size}:{capacity}")
 
 
+@pytest.mark.parametrize("batch", [16, 17])
+def test_later_rounds_at_the_order_limits(batch):
+    # 16 sequences fill every entry of the later rounds' sequence order; 17
+    # go without one (batch order).  With 128 or 136 groups the default
+    # launch has 2 slices per group in the first round and 8 in all, so a
+    # hit's band and tail get one slice.
+    w = workload("paged_b8", batch=batch, page_size=16, ctx_range=(300, 1500), steps=16, p_jump=0.15)
+    say(f"[order limits batch={batch}] {w}")
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp, capacity=30000)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"order_limits:{batch}")
+
+
 @pytest.mark.parametrize("name,period", [("8b_32k", 3), ("70b_128k", 3), ("tiny", 2)])
 def test_exact_ties_take_the_newest_entry(name, period):
     # q_t repeats q_{t-period} exactly, so several ring entries lie at
