@@ -304,38 +304,54 @@ def test_seeded_ring_every_step(name):
 # HIP graph replay
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["8b_32k_ragged", "paged_b8_small", "mqa_g32", "f32_d128_wide"])
-def test_graph_replays_equal_eager_steps(name):
+@pytest.mark.parametrize("name,capacity,stale", [("8b_32k_ragged", None, False),
+                                                  ("paged_b8_small", None, False),
+                                                  ("mqa_g32", None, False),
+                                                  ("f32_d128_wide", None, False),
+                                                  ("paged_b8_small", 70000, True)])
+def test_graph_replays_equal_eager_steps(name, capacity, stale):
     # one fused decode step is captured once and replayed for every token,
     # its input buffers refilled by eager copies between replays; every
     # replay must equal the eagerly launched step bitwise (the kernels read
-    # the lengths and ring counts on the device, so each replay advances)
+    # the lengths and ring counts on the device, so each replay advances).
+    # `stale`: a launch of four rounds captured before the prefill, so the
+    # later rounds' sequence order it holds is the batch order, not the
+    # order of the lengths the eager steps used: the results must not change
     from kv_cache_reuse_amd import binding as B
     from tests.gpu_harness import make_session
     base, kw = SMALL[name]
     w = workload(base, **{**kw, "steps": 12})
     inp = make_inputs(w)
-    ref = run_gpu(w, inp, fused=True)
+    ref = run_gpu(w, inp, fused=True, capacity=capacity)
     T = w.steps
     dev = torch.device("cuda")
-    sess = make_session(w, inp, T)
+    sess = make_session(w, inp, T, capacity=capacity)
     K, V = inp.k.to(dev), inp.v.to(dev)
     ctx = [int(c) for c in inp.contexts]
-    for b in range(w.batch):
-        sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
+    assert not stale or len(set(ctx)) > 1
     bidx = torch.arange(w.batch, device=dev)
     ctx_t = torch.tensor(ctx, device=dev)
     q_all = inp.q.to(dev)
     q_buf = torch.empty_like(q_all[0])
     k_buf = torch.empty((w.batch, w.n_kv_heads, w.head_dim), dtype=q_all.dtype, device=dev)
     v_buf = torch.empty_like(k_buf)
-    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        B.mac_decode_step_append(sess.ctx, q_buf.data_ptr(), k_buf.data_ptr(), v_buf.data_ptr(),
-                                 sess.k_cache.data_ptr(), sess.v_cache.data_ptr(), sess._pt(),
-                                 sess.out.data_ptr(), sess.match_ctx.data_ptr(),
-                                 sess.dist.data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    def capture():
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            B.mac_decode_step_append(sess.ctx, q_buf.data_ptr(), k_buf.data_ptr(), v_buf.data_ptr(),
+                                     sess.k_cache.data_ptr(), sess.v_cache.data_ptr(), sess._pt(),
+                                     sess.out.data_ptr(), sess.match_ctx.data_ptr(),
+                                     sess.dist.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+
+    if stale:
+        capture()
+    for b in range(w.batch):
+        sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
+    if not stale:
+        capture()
     torch.cuda.synchronize()
     for t in range(T):
         pos = ctx_t + t
