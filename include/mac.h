@@ -94,6 +94,21 @@ typedef struct {
   int32_t max_slices;        /* split-K slices per KV group; 0 = default     */
 } mac_config;
 
+/*
+ * Default slice count (max_slices = 0): base = ceil(256 / groups) slices per
+ * KV group, one workgroup per compute unit, where groups = batch * Hkv *
+ * ceil(G/16).  When a full-length sequence's base slices would hold more than
+ * about 6K keys, the launch takes further rounds of as many workgroups, one
+ * per 4096 keys a first-round slice would hold, at most 4 rounds.  The
+ * hardware deals the later rounds to compute units as they come free; on a
+ * step where a group's heads all hit, its later-round workgroups leave as
+ * soon as they read the group's plan, and for 2 to 16 sequences the later
+ * rounds visit the sequences longest first (by the host's length mirror at
+ * the call).  The count is capped by capacity / 64 + 1 and by
+ * G * slices <= 2048.  An explicit max_slices runs all its slices in one
+ * round.  The slice count fixes mac_workspace_bytes.
+ */
+
 typedef struct mac_ctx mac_ctx;
 
 /*
