@@ -104,9 +104,10 @@ typedef struct {
  * step where a group's heads all hit, its later-round workgroups leave as
  * soon as they read the group's plan, and for 2 to 16 sequences the later
  * rounds visit the sequences longest first (by the host's length mirror at
- * the call).  The count is capped by capacity / 64 + 1 and by
- * G * slices <= 2048.  An explicit max_slices runs all its slices in one
- * round.  The slice count fixes mac_workspace_bytes.
+ * the call).  The count is capped by ceil(capacity / 64) + 1, by 1024 and
+ * by G * slices <= 2048, and is at least 2.  An explicit max_slices (also
+ * capped by G * slices <= 2048) runs all its slices in one round.  The slice
+ * count fixes mac_workspace_bytes.
  */
 
 typedef struct mac_ctx mac_ctx;
