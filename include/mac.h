@@ -45,6 +45,12 @@
  *     device memory.  Ring and workspace are bound at mac_init and must stay
  *     allocated, and not be touched by the caller, until mac_destroy and
  *     every enqueued call using them has completed.
+ *   - The ring holds all of a context's state between steps (its entries and
+ *     the rotary table); it belongs to one context.  The workspace is scratch
+ *     of a single call: nothing in it outlives the call, so contexts created
+ *     with identical configs may share one workspace as long as their calls
+ *     never overlap (e.g. the layers of a model stepped in order on one
+ *     stream).  Calls that overlap on a shared workspace race.
  *   - Errors are returned as mac_status; mac_last_error() gives a message for
  *     the calling thread.  Argument checks happen before any HIP call, so a
  *     rejected call enqueues nothing.  A HIP error poisons the context: every
@@ -104,7 +110,9 @@ typedef struct {
  * step where a group's heads all hit, its later-round workgroups leave as
  * soon as they read the group's plan, and for 2 to 16 sequences the later
  * rounds visit the sequences longest first (by the host's length mirror at
- * the call).  The count is capped by ceil(capacity / 64) + 1, by 1024 and
+ * the call).  The early exit and the ordering apply to groups of at most 4
+ * query heads; wider groups run every later-round workgroup's match.  The
+ * count is capped by ceil(capacity / 64) + 1, by 1024 and
  * by G * slices <= 2048, and is at least 2.  An explicit max_slices (also
  * capped by G * slices <= 2048) runs all its slices in one round.  The slice
  * count fixes mac_workspace_bytes.
@@ -128,20 +136,40 @@ size_t mac_ring_bytes(const mac_config* cfg);      /* opaque ring            */
 size_t mac_workspace_bytes(const mac_config* cfg); /* opaque scratch         */
 
 /*
- * Create a context.
- *   ring          device, mac_ring_bytes(cfg); zeroed (emptied) here.
- *   workspace     device, mac_workspace_bytes(cfg); scratch for a step.
+ * Create a context (abstract: the match stage looks for similar queries in a
+ * short local window of recent ones; the ring is that window, W entries per
+ * sequence and query head, and it starts empty).
+ *   ring          device, mac_ring_bytes(cfg): the window's entries and the
+ *                 rotary table; emptied here.
+ *   workspace     device, mac_workspace_bytes(cfg): scratch of one call
+ *                 (see the conventions above for sharing it).
  *   seq_lens_dev  device int32[batch]: keys stored per sequence.  Device
  *                 truth, updated by the library's kernels.
  *   seq_lens_host host int32[batch]: the same lengths now; seeds the host
  *                 mirror used for capacity checks (no device sync needed).
- * The ring is emptied on `stream`.  Returns MAC_ERR_INVALID_ARG,
- * MAC_ERR_UNSUPPORTED, MAC_ERR_CAPACITY (a length beyond capacity) or
- * MAC_ERR_DEVICE.
+ * The ring is emptied and the rotary table written on `stream`.  Returns
+ * MAC_ERR_INVALID_ARG, MAC_ERR_UNSUPPORTED, MAC_ERR_CAPACITY (a length
+ * beyond capacity) or MAC_ERR_DEVICE.
  */
 mac_status mac_init(const mac_config* cfg, void* ring, void* workspace,
                     int32_t* seq_lens_dev, const int32_t* seq_lens_host,
                     void* stream, mac_ctx** out);
+
+/*
+ * Create a context that continues from a checkpoint.  A checkpoint of a
+ * context is a byte copy, taken with no call of it in flight, of its ring,
+ * its K and V caches, its page table (if paged) and seq_lens_dev, together
+ * with the lengths on the host.  mac_resume binds such copies (or the
+ * originals) under the same config: the ring's entries and push counts are
+ * kept as they are, the rotary table is rewritten, and the steps that
+ * follow give results bitwise identical to the steps the checkpointed
+ * context would have run.  Arguments and errors as for mac_init; the
+ * caller guarantees the ring was written by a context of the same config
+ * (the library cannot check a ring's contents).
+ */
+mac_status mac_resume(const mac_config* cfg, void* ring, void* workspace,
+                      int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                      void* stream, mac_ctx** out);
 
 /*
  * Append one token per sequence (abstract: "each token re-reads an
@@ -212,8 +240,9 @@ mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k
                                   void* stream);
 
 /*
- * Push entries into the rings directly (e.g. states computed at prefill so
- * that the first decode steps can match).  Device arrays indexed [b][h]:
+ * Push entries into the rings directly (abstract: the match stage's short
+ * local window of recent queries; e.g. states computed at prefill so that
+ * the first decode steps can match).  Device arrays indexed [b][h]:
  * q_pre [batch][Hq][d] dtype, o fp32 [batch][Hq][d] (normalized), m, l fp32
  * [batch][Hq] (natural log base), prefix_end, ctx_len int32 [batch][Hq].
  * mask uint8 [batch][Hq] or NULL (= push for every head).  The oldest entry

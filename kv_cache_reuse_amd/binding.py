@@ -31,7 +31,7 @@ MAC_DTYPE_BF16 = 1
 
 EXPORTED = (
     "mac_kv_cache_bytes", "mac_ring_bytes", "mac_workspace_bytes", "mac_init",
-    "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
+    "mac_resume", "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
     "mac_decode_step_append", "mac_seed_ring", "mac_query_cache_push", "mac_profile_enable",
     "mac_profile_read",
     "mac_destroy", "mac_last_error",
@@ -69,6 +69,7 @@ def _load():
         "mac_ring_bytes": (c_size_t, [POINTER(MacConfig)]),
         "mac_workspace_bytes": (c_size_t, [POINTER(MacConfig)]),
         "mac_init": (c_int, [POINTER(MacConfig), P, P, P, P, P, POINTER(c_void_p)]),
+        "mac_resume": (c_int, [POINTER(MacConfig), P, P, P, P, P, POINTER(c_void_p)]),
         "mac_append_kv": (c_int, [P, P, P, P, P, P, P]),
         "mac_prefill_kv": (c_int, [P, P, P, P, c_int32, P, P, c_int32, P]),
         "mac_read_kv": (c_int, [P, P, P, P, c_int32, c_int32, c_int32, P, P, P]),
@@ -124,6 +125,18 @@ def mac_init(cfg: MacConfig, ring: int, workspace: int, seq_lens_dev: int,
     out = c_void_p()
     _check(_lib.mac_init(ctypes.byref(cfg), ring, workspace, seq_lens_dev,
                          ctypes.cast(host, c_void_p), stream, ctypes.byref(out)))
+    return out.value
+
+
+def mac_resume(cfg: MacConfig, ring: int, workspace: int, seq_lens_dev: int,
+               seq_lens_host, stream: int) -> int:
+    """Like mac_init, but the ring's entries are kept (continuing from a
+    checkpoint).  Returns the context handle."""
+    n = cfg.batch
+    host = (c_int32 * n)(*[int(x) for x in seq_lens_host])
+    out = c_void_p()
+    _check(_lib.mac_resume(ctypes.byref(cfg), ring, workspace, seq_lens_dev,
+                           ctypes.cast(host, c_void_p), stream, ctypes.byref(out)))
     return out.value
 
 
@@ -209,7 +222,12 @@ class MacSession:
     the workspace, the device length array and, when paged, the page table.
     """
 
-    def __init__(self, cfg: MacConfig, device="cuda", page_table=None, stream=None):
+    def __init__(self, cfg: MacConfig, device="cuda", page_table=None, stream=None,
+                 workspace=None, resume_from=None):
+        """`workspace`: a uint8 device tensor of mac_workspace_bytes(cfg) to
+        use instead of a new one (contexts of identical configs whose calls
+        never overlap may share one).  `resume_from`: a checkpoint made by
+        `checkpoint()`; its buffers are adopted and bound with mac_resume."""
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -221,19 +239,30 @@ class MacSession:
             _lib.mac_kv_cache_bytes(ctypes.byref(cfg))
             raise MacError(MAC_ERR_INVALID_ARG, mac_last_error())
         es = 4 if cfg.dtype == MAC_DTYPE_F32 else 2
-        self.k_cache = torch.empty(kvb // es, dtype=self.dtype, device=self.device)
-        self.v_cache = torch.empty(kvb // es, dtype=self.dtype, device=self.device)
-        self.ring = torch.empty(mac_ring_bytes(cfg), dtype=torch.uint8, device=self.device)
-        self.workspace = torch.empty(mac_workspace_bytes(cfg), dtype=torch.uint8,
-                                     device=self.device)
-        self.seq_lens = torch.zeros(cfg.batch, dtype=torch.int32, device=self.device)
+        if workspace is None:
+            workspace = torch.empty(mac_workspace_bytes(cfg), dtype=torch.uint8,
+                                    device=self.device)
+        self.workspace = workspace
+        if resume_from is not None:
+            ck = resume_from
+            self.k_cache, self.v_cache = ck["k_cache"], ck["v_cache"]
+            self.ring, self.seq_lens = ck["ring"], ck["seq_lens"]
+            host = [int(x) for x in ck["seq_lens_host"]]
+            page_table = ck.get("page_table", page_table)
+        else:
+            self.k_cache = torch.empty(kvb // es, dtype=self.dtype, device=self.device)
+            self.v_cache = torch.empty(kvb // es, dtype=self.dtype, device=self.device)
+            self.ring = torch.empty(mac_ring_bytes(cfg), dtype=torch.uint8, device=self.device)
+            self.seq_lens = torch.zeros(cfg.batch, dtype=torch.int32, device=self.device)
+            host = [0] * cfg.batch
         self.page_table = None
         if cfg.page_size:
             if page_table is None:
                 raise ValueError("a paged config needs a page table")
             self.page_table = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
-        self.ctx = mac_init(cfg, self.ring.data_ptr(), self.workspace.data_ptr(),
-                            self.seq_lens.data_ptr(), [0] * cfg.batch, self._s())
+        bind = mac_resume if resume_from is not None else mac_init
+        self.ctx = bind(cfg, self.ring.data_ptr(), self.workspace.data_ptr(),
+                        self.seq_lens.data_ptr(), host, self._s())
         hq, d = cfg.n_q_heads, cfg.head_dim
         self.out = torch.empty((cfg.batch, hq, d), dtype=torch.float32, device=self.device)
         self.match_ctx = torch.empty((cfg.batch, hq), dtype=torch.int32, device=self.device)
@@ -300,6 +329,19 @@ class MacSession:
         mac_query_cache_push(self.ctx, q_pre.data_ptr(), o.data_ptr(), m.data_ptr(),
                              l.data_ptr(), prefix_end.data_ptr(), ctx_len.data_ptr(),
                              mask.data_ptr() if mask is not None else 0, self._s())
+
+    def checkpoint(self):
+        """Byte copies of everything a context carries between steps (ring,
+        caches, page table, lengths on device and host).  Synchronizes."""
+        t = self.torch
+        t.cuda.synchronize(self.device)
+        ck = {"ring": self.ring.clone(), "k_cache": self.k_cache.clone(),
+              "v_cache": self.v_cache.clone(), "seq_lens": self.seq_lens.clone()}
+        if self.page_table is not None:
+            ck["page_table"] = self.page_table.clone()
+        t.cuda.synchronize(self.device)
+        ck["seq_lens_host"] = ck["seq_lens"].cpu().tolist()
+        return ck
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

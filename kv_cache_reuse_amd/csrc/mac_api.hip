@@ -48,10 +48,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  // ring
-  size_t r_count, r_q, r_o, r_ml, r_pn, ring_bytes;
+  // ring: the entries, and the rotary table (per-context state kept beside
+  // them, so that the workspace holds nothing from one step to the next)
+  size_t r_count, r_q, r_o, r_ml, r_pn, r_invf, ring_bytes;
   // workspace
-  size_t w_po, w_pml, w_heads, w_reuse, w_pub, w_invf, w_out, w_save, ws_bytes;
+  size_t w_po, w_pml, w_heads, w_reuse, w_pub, w_out, w_save, ws_bytes;
   int slices;
   int first;            // slices per group in the first round of workgroups
   int64_t capacity;     // keys per sequence
@@ -122,6 +123,7 @@ Layout layout(const mac_config* c) {
   L.r_o = off;     off = align256(off + bh * slots * d * 4);
   L.r_ml = off;    off = align256(off + bh * slots * 2 * 4);
   L.r_pn = off;    off = align256(off + bh * slots * 2 * 4);
+  L.r_invf = off;  off = align256(off + (d / 2) * 8);
   L.ring_bytes = off;
 
   L.capacity = c->page_size ? (int64_t)c->max_pages_per_seq * mac::kTile : (int64_t)c->max_context;
@@ -163,7 +165,6 @@ Layout layout(const mac_config* c) {
   L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
   L.w_heads = off;   off = align256(off + bh * sizeof(mac::HeadState));
   L.w_reuse = off;   off = align256(off + bh * (d + 2) * 4);   // o rows, then (m, l) pairs
-  L.w_invf = off;  off = align256(off + (d / 2) * 8);
   L.w_out = off;   off = align256(off + bh * d * 4);          // ring seeding: discarded outputs
   L.w_save = off;  off = align256(off + (size_t)c->batch * 4); // ring seeding: saved lengths
   L.w_pub = off;   off = align256(off + (size_t)groups * 8);    // second round: published plans
@@ -262,8 +263,15 @@ size_t mac_workspace_bytes(const mac_config* cfg) {
   return layout(cfg).ws_bytes;
 }
 
-mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t* seq_lens_dev,
-                    const int32_t* seq_lens_host, void* stream, mac_ctx** out) {
+}  // extern "C"
+
+namespace {
+
+// mac_init (keep_ring false: the ring is emptied) and mac_resume (keep_ring
+// true: the ring's entries and counts are taken as they are).  Both write
+// the rotary table into the ring and clear the workspace's plan words.
+mac_status bind(const mac_config* cfg, void* ring, void* workspace, int32_t* seq_lens_dev,
+                const int32_t* seq_lens_host, void* stream, mac_ctx** out, bool keep_ring) {
   mac_status s;
   if (!out) return fail(MAC_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -285,21 +293,38 @@ mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t*
   ctx->ws = static_cast<char*>(workspace);
   ctx->seq_lens_dev = seq_lens_dev;
   ctx->mirror.assign(seq_lens_host, seq_lens_host + cfg->batch);
-  hipError_t e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
-                                      cfg->batch * cfg->n_q_heads, 0,
-                                      static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!keep_ring)
+    e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
+                             cfg->batch * cfg->n_q_heads, 0, st);
   if (e == hipSuccess)   // no published plan yet (all ones never matches a ring count)
     e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws + L.w_pub),
-                             (int)((L.ws_bytes - L.w_pub) / 4), -1, static_cast<hipStream_t>(stream));
+                             (int)((L.ws_bytes - L.w_pub) / 4), -1, st);
   if (e == hipSuccess)
-    e = mac::launch_inv_freq(reinterpret_cast<double*>(ctx->ws + L.w_invf), cfg->head_dim,
-                             cfg->rope_theta, static_cast<hipStream_t>(stream));
+    e = mac::launch_inv_freq(reinterpret_cast<double*>(ctx->ring + L.r_invf), cfg->head_dim,
+                             cfg->rope_theta, st);
   if (e != hipSuccess) {
     delete ctx;
-    return device_fail(nullptr, e, "mac_init: clearing the ring");
+    return device_fail(nullptr, e, keep_ring ? "mac_resume: binding the buffers"
+                                             : "mac_init: clearing the ring");
   }
   *out = ctx;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mac_status mac_init(const mac_config* cfg, void* ring, void* workspace, int32_t* seq_lens_dev,
+                    const int32_t* seq_lens_host, void* stream, mac_ctx** out) {
+  return bind(cfg, ring, workspace, seq_lens_dev, seq_lens_host, stream, out, false);
+}
+
+mac_status mac_resume(const mac_config* cfg, void* ring, void* workspace, int32_t* seq_lens_dev,
+                      const int32_t* seq_lens_host, void* stream, mac_ctx** out) {
+  return bind(cfg, ring, workspace, seq_lens_dev, seq_lens_host, stream, out, true);
 }
 
 mac_status mac_append_kv(mac_ctx* ctx, void* k_cache, void* v_cache, const int32_t* page_table,
@@ -379,7 +404,7 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.v_cache = v_cache;
   a.page_table = page_table;
   a.seq_lens = ctx->seq_lens_dev;
-  a.inv_freq = reinterpret_cast<const double*>(ctx->ws + L.w_invf);
+  a.inv_freq = reinterpret_cast<const double*>(ctx->ring + L.r_invf);
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.out = out;

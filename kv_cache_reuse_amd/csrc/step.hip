@@ -8,8 +8,15 @@
 // rest through a numerically stable merge); on a hit the cost does not depend
 // on the context length.
 //
-// Two launches per step, so that the only cross-workgroup hand-off goes
-// through a kernel boundary (no device-wide fences or atomics):
+// Two launches per step.  The partial states, the match records and the
+// reused ring states pass from the step kernel to the merge kernel through a
+// kernel boundary.  One hand-off stays inside the step kernel, and only in
+// launches with more than one round of workgroups: the group's slice-0
+// workgroup publishes its plan start (one 64-bit word, tagged with the ring
+// count of the group's first head) with an agent-scope atomic store, and a
+// later-round workgroup reads it with one plain 64-bit load; a word it reads
+// too early or stale fails the tag check, and the workgroup then matches as
+// usual.  The merge kernel clears the word after the step.
 //
 //  step_kernel, one workgroup per (slice, KV group), over a fixed number of
 //  slices S per group (the launch is the same for every step and can be
@@ -451,10 +458,14 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     const int cnt0 = a.ring.count[b * a.hq + kvh * G];
     // every lane decides (so every wave consumes the load); wave 0's
     // decision is the workgroup's
+    // (the word is all ones from the previous step's merge until slice 0
+    // publishes, so a read torn between the two values fails the tag check
+    // or the range check of the start, which is at most p_new)
     int leave = 0;
-    if (static_cast<unsigned>(pub >> 32) == static_cast<unsigned>(cnt0)) {
-      const Plan pp = make_plan(static_cast<int>(static_cast<unsigned>(pub)), n, a.band, a.part.S,
-                                a.part.first);
+    const unsigned lo_pub = static_cast<unsigned>(pub);
+    if (static_cast<unsigned>(pub >> 32) == static_cast<unsigned>(cnt0) &&
+        lo_pub <= static_cast<unsigned>(p_new)) {
+      const Plan pp = make_plan(static_cast<int>(lo_pub), n, a.band, a.part.S, a.part.first);
       leave = slice >= pp.n_pre + pp.n_post;
     }
     if (wave == 0 && lane == 0) sh.leave = leave;
@@ -1094,6 +1105,10 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
     // fused append: publish the new length (no kernel of this step reads it
     // after the step kernel)
     if (a.k_new && h == 0) a.seq_lens[b] = n;
+    // the group's published plan start is spent: clear it, so that every
+    // step begins with no plan published and no later step (of this context
+    // or of another one the workspace serves next) can take this one
+    if (hi == 0 && a.part.first < a.part.S) a.plan_pub[grp] = ~0ull;
   }
 }
 

@@ -95,10 +95,6 @@ class State:
     def empty(h: int, d: int) -> "State":
         return State(np.zeros((h, d)), np.full(h, NEG_INF), np.zeros(h))
 
-    def row(self, i: int) -> "State":
-        return State(self.o[i:i + 1].copy(), self.m[i:i + 1].copy(),
-                     self.l[i:i + 1].copy())
-
     @property
     def lse(self) -> np.ndarray:
         with np.errstate(divide="ignore"):
@@ -195,6 +191,13 @@ def match(q: np.ndarray, ring: Sequence[Entry], tau: float, p_new: int) -> Match
     return Match(best, bool(hit), best_d, dists)
 
 
+def fresh_start(entry: Entry) -> int:
+    """D8: on a hit, fresh attention starts where the matched entry's cached
+    prefix ends, so the band [entry.p, entry.n) is recomputed (amend) before
+    the tail [entry.n, n) (complete)."""
+    return entry.p
+
+
 def prefix_end(n: int, band: int) -> int:
     """D7/D8: the cached prefix of a query that saw n keys ends B keys early."""
     return max(0, n - band)
@@ -289,7 +292,7 @@ class MacOracle:
                 chosen[h] = ring[j]
                 res.hit[h] = True
                 res.match_n[h] = ring[j].n
-                res.s[h] = ring[j].p
+                res.s[h] = fresh_start(ring[j])
         res.keys_read[:] = n - res.s
 
         # fresh attention per KV group; query heads that share a start s are

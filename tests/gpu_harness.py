@@ -41,7 +41,7 @@ class GpuRun:
 
 
 def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] = None,
-                 capacity: Optional[int] = None):
+                 capacity: Optional[int] = None, workspace=None):
     from kv_cache_reuse_amd import binding as B
     paged = bool(w.page_size) if paged is None else paged
     if paged:
@@ -58,7 +58,82 @@ def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] 
         cfg = B.config_from_workload(w.replace(page_size=0),
                                      max_context=capacity or int(inp.contexts.max()) + steps,
                                      max_slices=max_slices)
-    return B.MacSession(cfg, page_table=table)
+    return B.MacSession(cfg, page_table=table, workspace=workspace)
+
+
+def step_inputs(w, inp, dev):
+    """The step inputs on the device: q [T, batch, Hq, d] and the appended
+    keys and values [T, batch, Hkv, d] of every step."""
+    K = inp.k.to(dev)
+    V = inp.v.to(dev)
+    T = inp.q.shape[0]
+    bidx = torch.arange(w.batch, device=dev)
+    pos = torch.tensor([int(c) for c in inp.contexts], device=dev)[:, None] + \
+        torch.arange(T, device=dev)[None]
+    k_new = K[bidx[:, None], :, pos].permute(1, 0, 2, 3).contiguous()
+    v_new = V[bidx[:, None], :, pos].permute(1, 0, 2, 3).contiguous()
+    return K, V, inp.q.to(dev).contiguous(), k_new, v_new
+
+
+def prefill(sess, w, inp, K, V):
+    for b in range(w.batch):
+        n0 = int(inp.contexts[b])
+        sess.prefill(b, K[b, :, :n0], V[b, :, :n0])
+
+
+def run_layers(w, inps, steps: Optional[int] = None, capacity: Optional[int] = None,
+               share_workspace: bool = False, graph: bool = False) -> List[GpuRun]:
+    """Several contexts of one config (say the layers of a model), each with
+    its own caches, rings and inputs, stepped in order for every token on one
+    stream with fused append+decode calls.  `share_workspace`: every context
+    uses the first one's workspace.  `graph`: all steps of all contexts are
+    captured in one HIP graph, which is replayed once; each (step, context)
+    writes outputs of its own, checked after the replay."""
+    from kv_cache_reuse_amd import binding as B
+    T = inps[0].q.shape[0] if steps is None else steps
+    dev = torch.device("cuda")
+    sessions, staged = [], []
+    for inp in inps:
+        ws = sessions[0].workspace if (share_workspace and sessions) else None
+        sess = make_session(w, inp, T, capacity=capacity, workspace=ws)
+        K, V, q, kn, vn = step_inputs(w, inp, dev)
+        prefill(sess, w, inp, K, V)
+        sessions.append(sess)
+        staged.append((q, kn, vn))
+    hq = w.n_q_heads
+    outs = [torch.empty((T, w.batch, hq, w.head_dim), dtype=torch.float32, device=dev)
+            for _ in inps]
+    mns = [torch.empty((T, w.batch, hq), dtype=torch.int32, device=dev) for _ in inps]
+    dss = [torch.empty((T, w.batch, hq), dtype=torch.float32, device=dev) for _ in inps]
+    torch.cuda.synchronize()
+
+    def all_steps(stream):
+        for t in range(T):
+            for i, sess in enumerate(sessions):
+                q, kn, vn = staged[i]
+                B.mac_decode_step_append(sess.ctx, q[t].data_ptr(), kn[t].data_ptr(),
+                                         vn[t].data_ptr(), sess.k_cache.data_ptr(),
+                                         sess.v_cache.data_ptr(), sess._pt(),
+                                         outs[i][t].data_ptr(), mns[i][t].data_ptr(),
+                                         dss[i][t].data_ptr(), stream)
+
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            all_steps(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del g
+    else:
+        all_steps(sessions[0]._s())
+        torch.cuda.synchronize()
+    runs = []
+    for i, sess in enumerate(sessions):
+        o, m, d = outs[i].cpu().numpy(), mns[i].cpu().numpy(), dss[i].cpu().numpy()
+        runs.append(GpuRun({t: o[t] for t in range(T)}, {t: m[t] for t in range(T)},
+                           {t: d[t] for t in range(T)}, sess))
+    return runs
 
 
 def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 0,

@@ -137,3 +137,17 @@ def test_host_integer_logic(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "OK" in r.stdout, r.stdout[-2000:]
+
+
+def test_device_error_poisons_the_context(tmp_path):
+    # the C ABI linked against launchers that fail on request (no GPU):
+    # MAC_ERR_DEVICE from the failing call, MAC_ERR_STATE from every later
+    # call on that context, other contexts unaffected
+    exe = str(tmp_path / "state_stub_test")
+    srcs = [os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", "mac_api.hip"),
+            os.path.join(ROOT, "tests", "cpp", "state_stub.cpp")]
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O1", "-std=c++17",
+                        *srcs, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]

@@ -74,6 +74,10 @@ MUTANTS = [
     ("merge", merge_without_rescale, [lambda: P.test_merge_of_any_partition_equals_single_pass(1.0)]),
     ("attend", attend_wrong_scale, [P.test_attend_equals_scipy_softmax_attention]),
     ("match", match_oldest_on_ties, [P.test_match_golden_ties_and_strictness]),
+    # a hit that skips the band: fresh attention from the matched entry's
+    # context end instead of its prefix end
+    ("fresh_start", lambda e: e.n,
+     [P.test_hit_reads_golden, lambda: P.test_brute_force_agrees_on_tiny_inputs(0)]),
     ("prefix_end", lambda n, band: max(0, n - band + 1),
      [lambda: P.test_brute_force_agrees_on_tiny_inputs(0)]),
     ("prefix_end", lambda n, band: max(0, n - band - 1),
