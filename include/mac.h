@@ -142,7 +142,10 @@ size_t mac_workspace_bytes(const mac_config* cfg); /* opaque scratch         */
  *   ring          device, mac_ring_bytes(cfg): the window's entries and the
  *                 rotary table; emptied here.
  *   workspace     device, mac_workspace_bytes(cfg): scratch of one call
- *                 (see the conventions above for sharing it).
+ *                 (see the conventions above for sharing it); may be NULL
+ *                 for a context stepped only by
+ *                 mac_decode_step_append_noalloc (the other decode entry
+ *                 points and mac_seed_ring then return MAC_ERR_INVALID_ARG).
  *   seq_lens_dev  device int32[batch]: keys stored per sequence.  Device
  *                 truth, updated by the library's kernels.
  *   seq_lens_host host int32[batch]: the same lengths now; seeds the host
@@ -238,6 +241,31 @@ mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k
                                   const int32_t* page_table, float* out,
                                   int32_t* match_ctx_out, float* dist_out,
                                   void* stream);
+
+/*
+ * mac_decode_step_append for callers that cannot allocate device memory at
+ * the call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): same arguments, results bitwise identical, and it
+ * calls no allocating routine.  The step's scratch (partial states, match
+ * records, reused ring states, published plan starts) lives in a static
+ * device array of the library, 8 MiB per GPU, held until the process ends,
+ * instead of the context's workspace; so a context used only through this
+ * entry point may be created with workspace = NULL.  The array is found at
+ * mac_init / mac_resume, once per device.  A config whose step needs more
+ * (32 KiB of plan words plus the part of mac_workspace_bytes before the
+ * ring-seeding scratch: for G = 4, d = 128 about 2 KiB per (KV group,
+ * slice); at most 4096 KV groups) is refused with MAC_ERR_CAPACITY before
+ * any device call.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads, other contexts)
+ * race and must be serialized by the caller.  Kernel timing
+ * (mac_profile_enable) does not apply to this entry point.
+ */
+mac_status mac_decode_step_append_noalloc(mac_ctx* ctx, const void* q_pre,
+                                          const void* k_new, const void* v_new,
+                                          void* k_cache, void* v_cache,
+                                          const int32_t* page_table, float* out,
+                                          int32_t* match_ctx_out,
+                                          float* dist_out, void* stream);
 
 /*
  * Push entries into the rings directly (abstract: the match stage's short

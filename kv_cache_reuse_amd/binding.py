@@ -32,7 +32,7 @@ MAC_DTYPE_BF16 = 1
 EXPORTED = (
     "mac_kv_cache_bytes", "mac_ring_bytes", "mac_workspace_bytes", "mac_init",
     "mac_resume", "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
-    "mac_decode_step_append", "mac_seed_ring", "mac_query_cache_push", "mac_profile_enable",
+    "mac_decode_step_append", "mac_decode_step_append_noalloc", "mac_seed_ring", "mac_query_cache_push", "mac_profile_enable",
     "mac_profile_read",
     "mac_destroy", "mac_last_error",
 )
@@ -75,6 +75,7 @@ def _load():
         "mac_read_kv": (c_int, [P, P, P, P, c_int32, c_int32, c_int32, P, P, P]),
         "mac_decode_step": (c_int, [P, P, P, P, P, P, P, P, P]),
         "mac_decode_step_append": (c_int, [P, P, P, P, P, P, P, P, P, P, P]),
+        "mac_decode_step_append_noalloc": (c_int, [P, P, P, P, P, P, P, P, P, P, P]),
         "mac_seed_ring": (c_int, [P, P, c_int32, P, P, P, P]),
         "mac_query_cache_push": (c_int, [P, P, P, P, P, P, P, P, P]),
         "mac_profile_enable": (c_int, [P, c_int]),
@@ -167,6 +168,13 @@ def mac_decode_step_append(ctx, q_pre, k_new, v_new, k_cache, v_cache, page_tabl
                                        dist_out or None, stream))
 
 
+def mac_decode_step_append_noalloc(ctx, q_pre, k_new, v_new, k_cache, v_cache, page_table,
+                                   out, match_ctx_out, dist_out, stream):
+    _check(_lib.mac_decode_step_append_noalloc(ctx, q_pre, k_new, v_new, k_cache, v_cache,
+                                               page_table or None, out, match_ctx_out or None,
+                                               dist_out or None, stream))
+
+
 def mac_seed_ring(ctx, q_hist, n_hist, k_cache, v_cache, page_table, stream):
     _check(_lib.mac_seed_ring(ctx, q_hist, n_hist, k_cache, v_cache, page_table or None, stream))
 
@@ -223,11 +231,13 @@ class MacSession:
     """
 
     def __init__(self, cfg: MacConfig, device="cuda", page_table=None, stream=None,
-                 workspace=None, resume_from=None):
+                 workspace=None, resume_from=None, no_workspace=False):
         """`workspace`: a uint8 device tensor of mac_workspace_bytes(cfg) to
         use instead of a new one (contexts of identical configs whose calls
-        never overlap may share one).  `resume_from`: a checkpoint made by
-        `checkpoint()`; its buffers are adopted and bound with mac_resume."""
+        never overlap may share one).  `no_workspace`: bind none (the context
+        can then step only through mac_decode_step_append_noalloc).
+        `resume_from`: a checkpoint made by `checkpoint()`; its buffers are
+        adopted and bound with mac_resume."""
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -239,7 +249,7 @@ class MacSession:
             _lib.mac_kv_cache_bytes(ctypes.byref(cfg))
             raise MacError(MAC_ERR_INVALID_ARG, mac_last_error())
         es = 4 if cfg.dtype == MAC_DTYPE_F32 else 2
-        if workspace is None:
+        if workspace is None and not no_workspace:
             workspace = torch.empty(mac_workspace_bytes(cfg), dtype=torch.uint8,
                                     device=self.device)
         self.workspace = workspace
@@ -261,7 +271,8 @@ class MacSession:
                 raise ValueError("a paged config needs a page table")
             self.page_table = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
         bind = mac_resume if resume_from is not None else mac_init
-        self.ctx = bind(cfg, self.ring.data_ptr(), self.workspace.data_ptr(),
+        self.ctx = bind(cfg, self.ring.data_ptr(),
+                        self.workspace.data_ptr() if self.workspace is not None else 0,
                         self.seq_lens.data_ptr(), host, self._s())
         hq, d = cfg.n_q_heads, cfg.head_dim
         self.out = torch.empty((cfg.batch, hq, d), dtype=torch.float32, device=self.device)
@@ -307,6 +318,19 @@ class MacSession:
                                self.k_cache.data_ptr(), self.v_cache.data_ptr(), self._pt(),
                                out.data_ptr(), mc.data_ptr() if mc is not None else 0,
                                ds.data_ptr() if ds is not None else 0, self._s())
+        return out, mc, ds
+
+    def decode_append_noalloc(self, q_pre, k_new, v_new, out=None, match_ctx=True, dist=True):
+        """decode_append through mac_decode_step_append_noalloc (the step's
+        scratch is the library's static device array)."""
+        out = self.out if out is None else out
+        mc = self.match_ctx if match_ctx else None
+        ds = self.dist if dist else None
+        mac_decode_step_append_noalloc(self.ctx, q_pre.data_ptr(), k_new.data_ptr(),
+                                       v_new.data_ptr(), self.k_cache.data_ptr(),
+                                       self.v_cache.data_ptr(), self._pt(), out.data_ptr(),
+                                       mc.data_ptr() if mc is not None else 0,
+                                       ds.data_ptr() if ds is not None else 0, self._s())
         return out, mc, ds
 
     def read_kv(self, seq: int, start: int, count: int):

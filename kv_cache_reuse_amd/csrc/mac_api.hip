@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -46,6 +47,29 @@ constexpr int kMaxRounds = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------ static scratch (noalloc) --
+// mac_decode_step_append_noalloc keeps the scratch of a step in this array
+// instead of the context's workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  Layout: kScratchPlanGroups plan words
+// (all ones between steps), then the step scratch a workspace starts with
+// (partial states, match records, reused ring states).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kScratchPlanGroups = 4096;
+constexpr size_t kScratchStepOffset = size_t(kScratchPlanGroups) * 8;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The array's device address on each device, resolved once per device (with
+// that device current) by the first mac_init / mac_resume on it.  In host
+// code `scratch` names a host-side stand-in: only these addresses are used.
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  bool resolved = false;
+  hipError_t err = hipSuccess;
+  char* ptr = nullptr;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
 
 struct Layout {
   // ring: the entries, and the rotary table (per-context state kept beside
@@ -183,6 +207,8 @@ struct mac_ctx {
   std::vector<int64_t> mirror;
   bool poisoned = false;
   bool profiling = false;
+  char* scratch = nullptr;          // this device's static scratch, or null
+  hipError_t scratch_err = hipSuccess;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
   size_t ev_used = 0;
 
@@ -267,6 +293,37 @@ size_t mac_workspace_bytes(const mac_config* cfg) {
 
 namespace {
 
+// The current device's static scratch: resolved on the first call for the
+// device, its plan words set to all ones (synchronously, so that a context
+// on another stream cannot step before that), and kept.  Returns the
+// address, or null with *err set.
+char* device_scratch(hipStream_t st, hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (!sl.resolved) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess)
+      e = mac::launch_fill_i32(static_cast<int32_t*>(p), kScratchPlanGroups * 2, -1, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    sl.resolved = true;
+    sl.err = e;
+    sl.ptr = e == hipSuccess ? static_cast<char*>(p) : nullptr;
+  }
+  *err = sl.err;
+  return sl.ptr;
+}
+
 // mac_init (keep_ring false: the ring is emptied) and mac_resume (keep_ring
 // true: the ring's entries and counts are taken as they are).  Both write
 // the rotary table into the ring and clear the workspace's plan words.
@@ -277,7 +334,7 @@ mac_status bind(const mac_config* cfg, void* ring, void* workspace, int32_t* seq
   *out = nullptr;
   if ((s = check_config(cfg))) return s;
   if ((s = check_ptr(ring, "ring"))) return s;
-  if ((s = check_ptr(workspace, "workspace"))) return s;
+  if ((s = check_ptr(workspace, "workspace", false))) return s;
   if ((s = check_ptr(seq_lens_dev, "seq_lens_dev"))) return s;
   if (!seq_lens_host) return fail(MAC_ERR_INVALID_ARG, "seq_lens_host is NULL");
   const Layout L = layout(cfg);
@@ -298,7 +355,7 @@ mac_status bind(const mac_config* cfg, void* ring, void* workspace, int32_t* seq
   if (!keep_ring)
     e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ring + L.r_count),
                              cfg->batch * cfg->n_q_heads, 0, st);
-  if (e == hipSuccess)   // no published plan yet (all ones never matches a ring count)
+  if (e == hipSuccess && ctx->ws)   // no published plan yet (all ones never matches a ring count)
     e = mac::launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws + L.w_pub),
                              (int)((L.ws_bytes - L.w_pub) / 4), -1, st);
   if (e == hipSuccess)
@@ -309,6 +366,9 @@ mac_status bind(const mac_config* cfg, void* ring, void* workspace, int32_t* seq
     return device_fail(nullptr, e, keep_ring ? "mac_resume: binding the buffers"
                                              : "mac_init: clearing the ring");
   }
+  // the static scratch of mac_decode_step_append_noalloc; a failure here is
+  // reported by that entry point (the workspace entry points do not need it)
+  ctx->scratch = device_scratch(st, &ctx->scratch_err);
   *out = ctx;
   return ok();
 }
@@ -392,10 +452,12 @@ mac_status mac_read_kv(mac_ctx* ctx, const void* k_cache, const void* v_cache,
 
 namespace {
 
-// Shared body of mac_decode_step and mac_decode_step_append (k_new != null).
 // Kernel arguments of one step; fused-append and optional outputs unset.
+// The step's scratch (partial states, match records, reused states) is
+// carved from `base` at the workspace's offsets, the plan words are `pub`.
 mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, const void* v_cache,
-                        const int32_t* page_table, float* out) {
+                        const int32_t* page_table, float* out, char* base,
+                        unsigned long long* pub) {
   const mac_config& c = ctx->cfg;
   const Layout& L = ctx->L;
   mac::StepArgs a;
@@ -410,13 +472,13 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   a.out = out;
   a.match_ctx_out = nullptr;
   a.dist_out = nullptr;
-  a.heads = reinterpret_cast<mac::HeadState*>(ctx->ws + L.w_heads);
-  a.reuse_o = reinterpret_cast<float*>(ctx->ws + L.w_reuse);
-  a.plan_pub = reinterpret_cast<unsigned long long*>(ctx->ws + L.w_pub);
+  a.heads = reinterpret_cast<mac::HeadState*>(base + L.w_heads);
+  a.reuse_o = reinterpret_cast<float*>(base + L.w_reuse);
+  a.plan_pub = pub;
   a.part.first = L.first;
   a.reuse_ml = a.reuse_o + (size_t)c.batch * c.n_q_heads * c.head_dim;
-  a.part.o = reinterpret_cast<float*>(ctx->ws + L.w_po);
-  a.part.ml = reinterpret_cast<float*>(ctx->ws + L.w_pml);
+  a.part.o = reinterpret_cast<float*>(base + L.w_po);
+  a.part.ml = reinterpret_cast<float*>(base + L.w_pml);
   a.part.S = L.slices;
   a.ring = ctx->ring_view();
   a.geom = ctx->geom();
@@ -442,11 +504,38 @@ mac::StepArgs step_args(mac_ctx* ctx, const void* q_pre, const void* k_cache, co
   return a;
 }
 
+// Shared body of the decode entry points (k_new != null: fused append).
+// noalloc: the step's scratch is the device's static array, not the
+// workspace, and nothing is allocated (no timing events either).
 mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, const void* v_cache,
                        const int32_t* page_table, float* out, int32_t* match_ctx_out,
-                       float* dist_out, const void* k_new, const void* v_new, void* stream) {
+                       float* dist_out, const void* k_new, const void* v_new, void* stream,
+                       bool noalloc = false) {
   mac_status s;
   if ((s = check_ctx(ctx))) return s;
+  char* base;
+  unsigned long long* pub;
+  if (noalloc) {
+    const int groups = ctx->cfg.batch * ctx->cfg.n_kv_heads * n_chunks(&ctx->cfg);
+    const size_t need = kScratchStepOffset + ctx->L.w_out;
+    if (groups > kScratchPlanGroups || need > kScratchBytes)
+      return fail(MAC_ERR_CAPACITY, "mac_decode_step_append_noalloc: the step needs %zu bytes "
+                  "of static scratch for %d KV groups; the library holds %zu bytes and %d groups "
+                  "(use mac_decode_step_append with a workspace)", need, groups, kScratchBytes,
+                  kScratchPlanGroups);
+    if (!ctx->scratch)
+      return fail(MAC_ERR_DEVICE, "mac_decode_step_append_noalloc: the static scratch of this "
+                  "device is unavailable: HIP error %d (%s)", (int)ctx->scratch_err,
+                  hipGetErrorString(ctx->scratch_err));
+    base = ctx->scratch + kScratchStepOffset;
+    pub = reinterpret_cast<unsigned long long*>(ctx->scratch);
+  } else {
+    if (!ctx->ws)
+      return fail(MAC_ERR_INVALID_ARG, "this context was created without a workspace: use "
+                  "mac_decode_step_append_noalloc");
+    base = ctx->ws;
+    pub = reinterpret_cast<unsigned long long*>(ctx->ws + ctx->L.w_pub);
+  }
   if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
   if ((s = check_ptr(q_pre, "q_pre"))) return s;
   if ((s = check_ptr(out, "out"))) return s;
@@ -466,14 +555,14 @@ mac_status decode_impl(mac_ctx* ctx, const void* q_pre, const void* k_cache, con
   }
 
   const mac_config& c = ctx->cfg;
-  mac::StepArgs a = step_args(ctx, q_pre, k_cache, v_cache, page_table, out);
+  mac::StepArgs a = step_args(ctx, q_pre, k_cache, v_cache, page_table, out, base, pub);
   a.k_new = k_new;
   a.v_new = v_new;
   a.match_ctx_out = match_ctx_out;
   a.dist_out = dist_out;
 
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (ctx->profiling && ctx->ev_used < 65536) {
+  if (ctx->profiling && !noalloc && ctx->ev_used < 65536) {
     if (ctx->ev_used == ctx->events.size()) {
       // timing only (read after the stream has been synchronized): no
       // system-scope fence, whose cache write-back and invalidation would
@@ -518,6 +607,17 @@ mac_status mac_decode_step_append(mac_ctx* ctx, const void* q_pre, const void* k
                      k_new, v_new, stream);
 }
 
+mac_status mac_decode_step_append_noalloc(mac_ctx* ctx, const void* q_pre, const void* k_new,
+                                          const void* v_new, void* k_cache, void* v_cache,
+                                          const int32_t* page_table, float* out,
+                                          int32_t* match_ctx_out, float* dist_out, void* stream) {
+  mac_status s;
+  if ((s = check_ctx(ctx))) return s;
+  if (!k_new || !v_new) return fail(MAC_ERR_INVALID_ARG, "k_new and v_new are required");
+  return decode_impl(ctx, q_pre, k_cache, v_cache, page_table, out, match_ctx_out, dist_out,
+                     k_new, v_new, stream, true);
+}
+
 mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist, const void* k_cache,
                          const void* v_cache, const int32_t* page_table, void* stream) {
   mac_status s;
@@ -526,6 +626,7 @@ mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist, const voi
   if (n_hist < 0 || n_hist > c.window)
     return fail(MAC_ERR_INVALID_ARG, "n_hist must be in [0, W = %d] (got %d)", c.window, n_hist);
   if (n_hist == 0) return ok();
+  if (!ctx->ws) return fail(MAC_ERR_INVALID_ARG, "mac_seed_ring needs a context with a workspace");
   if ((s = check_kv(ctx, k_cache, v_cache, page_table))) return s;
   if ((s = check_ptr(q_hist, "q_hist"))) return s;
   for (int b = 0; b < c.batch; ++b)
@@ -538,7 +639,8 @@ mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist, const voi
   // a miss there would have pushed.  Outputs land in the workspace.
   const Layout& L = ctx->L;
   mac::StepArgs a = step_args(ctx, q_hist, k_cache, v_cache, page_table,
-                              reinterpret_cast<float*>(ctx->ws + L.w_out));
+                              reinterpret_cast<float*>(ctx->ws + L.w_out), ctx->ws,
+                              reinterpret_cast<unsigned long long*>(ctx->ws + L.w_pub));
   a.tau2 = -1.0f;
   int32_t* saved = reinterpret_cast<int32_t*>(ctx->ws + L.w_save);
   const hipStream_t st = static_cast<hipStream_t>(stream);
