@@ -71,6 +71,7 @@ class Workload:
     page_size: int = 0         # 0 = contiguous cache, else keys per page
     ctx_range: Optional[tuple] = None   # (lo, hi) inclusive, per sequence
     rho_range: Optional[tuple] = None   # (lo, hi) uniform, per query head
+    rho_per_kv: bool = False   # rho_range drawn per KV head, shared by its query heads
     outlier_p: float = 0.0
     outlier_scale: float = 1.0
     period: int = 0            # >0: q_t repeats q_{t-period} exactly (tests)
@@ -160,10 +161,14 @@ def contexts(w: Workload, layer: int = 0) -> np.ndarray:
 
 
 def rho_per_head(w: Workload, layer: int = 0) -> np.ndarray:
+    """AR(1) coefficient of each query head: w.rho, or drawn uniformly from
+    w.rho_range per query head (or per KV head, shared by its query heads)."""
     if w.rho_range is None:
         return np.full(w.n_q_heads, w.rho, dtype=np.float64)
     rng = np.random.default_rng(_children(w, layer)["rho"])
     lo, hi = w.rho_range
+    if w.rho_per_kv:
+        return np.repeat(rng.uniform(lo, hi, size=w.n_kv_heads), w.group)
     return rng.uniform(lo, hi, size=w.n_q_heads)
 
 
@@ -213,31 +218,41 @@ class Inputs:
         return self.contexts + self.q.shape[0]
 
 
+def make_kv_group(w: Workload, ctx: np.ndarray, steps: int, b: int, g: int, layer: int = 0):
+    """Keys and values of one (sequence, KV head) for prefill plus every
+    decode step: ([n, d] dtype tensor, [n, d] dtype tensor, [n] bool outlier
+    flags or None) with n = ctx[b] + steps.  Each group draws from seeds of
+    its own, so a group can be drawn without the others."""
+    ch = _children(w, layer)
+    i = b * w.n_kv_heads + g
+    n = int(ctx[b]) + steps
+    kk = np.random.default_rng(ch["k"].spawn(w.batch * w.n_kv_heads)[i]).standard_normal(
+        (n, w.head_dim), dtype=np.float32)
+    flag = None
+    if w.outlier_p > 0:
+        oss = ch["outlier"].spawn(w.batch * w.n_kv_heads)[i]
+        flag = np.random.default_rng(oss).random(n) < w.outlier_p
+        kk[flag] *= np.float32(w.outlier_scale)
+    vv = np.random.default_rng(ch["v"].spawn(w.batch * w.n_kv_heads)[i]).standard_normal(
+        (n, w.head_dim), dtype=np.float32)
+    return _round(kk, w.dtype), _round(vv, w.dtype), flag
+
+
 def make_kv(w: Workload, ctx: np.ndarray, steps: int, layer: int = 0):
     """Keys and values for prefill plus every decode step, natural layout."""
-    ch = _children(w, layer)
     L = int(ctx.max()) + steps
     shape = (w.batch, w.n_kv_heads, L, w.head_dim)
     k = torch.zeros(shape, dtype=w.torch_dtype())
     v = torch.zeros(shape, dtype=w.torch_dtype())
-    kss = ch["k"].spawn(w.batch * w.n_kv_heads)
-    vss = ch["v"].spawn(w.batch * w.n_kv_heads)
-    oss = ch["outlier"].spawn(w.batch * w.n_kv_heads)
     outl = np.zeros((w.batch, w.n_kv_heads, L), dtype=bool) if w.outlier_p > 0 else None
     for b in range(w.batch):
         n = int(ctx[b]) + steps
         for g in range(w.n_kv_heads):
-            i = b * w.n_kv_heads + g
-            kk = np.random.default_rng(kss[i]).standard_normal(
-                (n, w.head_dim), dtype=np.float32)
+            kk, vv, flag = make_kv_group(w, ctx, steps, b, g, layer)
+            k[b, g, :n] = kk
+            v[b, g, :n] = vv
             if outl is not None:
-                flag = np.random.default_rng(oss[i]).random(n) < w.outlier_p
-                kk[flag] *= np.float32(w.outlier_scale)
                 outl[b, g, :n] = flag
-            k[b, g, :n] = _round(kk, w.dtype)
-            vv = np.random.default_rng(vss[i]).standard_normal(
-                (n, w.head_dim), dtype=np.float32)
-            v[b, g, :n] = _round(vv, w.dtype)
     return k, v, outl
 
 

@@ -1,16 +1,6 @@
 """Shared GPU-test plumbing: run a synthetic workload through libmac and
-compare it with the fp64 oracle.
-
-The oracle runs per KV group (b, g): the G query heads of that group form an
-independent problem (their own rings, their own keys), so a sample of groups
-can be checked at full size without replaying the whole batch.
-
-Decision parity: hit/miss and the matched entry's context length must agree
-exactly, except where the oracle's best distance lies within 1e-4 * tau of
-tau, or (both sides hitting) the GPU's entry is within 1e-4 * tau of the
-oracle's best: there the GPU's decision is accepted, logged, and the oracle
-follows it so that both rings stay comparable.
-"""
+record its outputs for the comparison with the fp64 oracle
+(tests/oracle_check.py, re-exported here)."""
 
 from __future__ import annotations
 
@@ -21,10 +11,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from oracle import mac_oracle as M
-
-OUT_TOL = 2e-3          # max |out_gpu - out_oracle|
-BORDER_REL = 1e-4       # borderline band around tau, relative
+from tests.oracle_check import (BORDER_REL, OUT_TOL, Report, check_groups,  # noqa: F401
+                                check_groups_parallel)
 
 
 def say(msg: str) -> None:
@@ -175,90 +163,3 @@ def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 
             res.dist[t] = ds.cpu().numpy().copy()
     torch.cuda.synchronize()
     return res
-
-
-@dataclasses.dataclass
-class Report:
-    steps: int = 0
-    heads: int = 0
-    hits: int = 0
-    borderline: List[tuple] = dataclasses.field(default_factory=list)
-    max_err: float = 0.0
-    max_dist_err: float = 0.0
-    mismatches: List[tuple] = dataclasses.field(default_factory=list)
-
-    def ok(self, tol=OUT_TOL) -> bool:
-        return not self.mismatches and self.max_err <= tol
-
-
-def check_groups(w, inp, gpu: GpuRun, groups: Sequence[Tuple[int, int]],
-                 steps: Optional[Sequence[int]] = None, K64=None, V64=None,
-                 tol: float = OUT_TOL, seed_q64=None, collect=None) -> Report:
-    """Replay the oracle for each KV group (b, g) over every step 0..T-1 and
-    compare the recorded GPU steps.  `gpu` must hold every step for exact
-    decision checks; steps missing from it are replayed without comparing.
-    With `collect` (a dict), the oracle's outputs and decisions are stored in
-    it under (b, g, t)."""
-    T = max(gpu.out) + 1 if steps is None else max(steps) + 1
-    G = w.group
-    rep = Report()
-    tau = float(w.tau)
-    for (b, g) in groups:
-        orc = M.MacOracle(1, G, 1, w.head_dim, w.window, w.band, tau, w.rope_theta)
-        Kg = (K64[b, g] if K64 is not None else inp.k[b, g].double().numpy())[None]
-        Vg = (V64[b, g] if V64 is not None else inp.v[b, g].double().numpy())[None]
-        heads = list(range(g * G, (g + 1) * G))
-        if seed_q64 is not None:
-            orc.seed(0, seed_q64[:, b, heads], Kg, Vg, int(inp.contexts[b]))
-        for t in range(T):
-            n = int(inp.contexts[b]) + t + 1
-            p_new = max(0, n - w.band)
-            q = inp.q64[t, b, heads]
-            have = t in gpu.out
-            force = {}
-            if have:
-                for i, h in enumerate(heads):
-                    mt = M.match(q[i], orc.rings[0][i], tau, p_new)
-                    g_n = int(gpu.match_n[t][b, h])
-                    g_hit = g_n >= 0
-                    o_n = orc.rings[0][i][mt.j].n if mt.hit else -1
-                    # distance of the GPU-reported best candidate
-                    gd = float(gpu.dist[t][b, h])
-                    if np.isfinite(mt.dist):
-                        rep.max_dist_err = max(rep.max_dist_err,
-                                               abs(gd - mt.dist) / max(1.0, mt.dist))
-                    if g_hit == mt.hit and g_n == o_n:
-                        continue
-                    border = abs(mt.dist - tau) <= BORDER_REL * tau
-                    j_gpu = -1
-                    if g_hit:
-                        js = [j for j, e in enumerate(orc.rings[0][i]) if e.n == g_n]
-                        j_gpu = js[0] if js else -1
-                        if j_gpu >= 0 and mt.hit:
-                            dj = mt.dists[j_gpu]
-                            border = border or abs(dj - mt.dist) <= BORDER_REL * tau
-                        if j_gpu >= 0 and not mt.hit:
-                            dj = mt.dists[j_gpu]
-                            border = border or abs(dj - tau) <= BORDER_REL * tau
-                    if border and (not g_hit or j_gpu >= 0):
-                        rep.borderline.append((b, h, t, mt.dist, g_n, o_n))
-                        force[i] = (g_hit, j_gpu)
-                    else:
-                        rep.mismatches.append((b, h, t, "decision", g_n, o_n, mt.dist, gd))
-            r = orc.step(0, q, Kg, Vg, n, force=force or None)
-            if collect is not None:
-                collect[(b, g, t)] = (r.out.copy(), r.match_n.copy())
-            if have:
-                err = np.abs(gpu.out[t][b, heads].astype(np.float64) - r.out)
-                e = float(np.nanmax(err)) if err.size else 0.0
-                nan_gpu = np.isnan(gpu.out[t][b, heads])
-                nan_orc = np.isnan(r.out)
-                if (nan_gpu != nan_orc).any():
-                    rep.mismatches.append((b, g, t, "nan-pattern"))
-                rep.max_err = max(rep.max_err, e)
-                if e > tol:
-                    rep.mismatches.append((b, g, t, "out", e))
-                rep.steps += 1
-                rep.heads += G
-                rep.hits += int(r.hit.sum())
-    return rep

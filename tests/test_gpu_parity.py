@@ -2,8 +2,9 @@
 
 Small shapes (several 16-token tiles, ragged tails, every KV group) are
 checked on every step; the full-size shapes run in the launch configuration
-the benchmark uses and are checked on sampled KV groups, the oracle
-replaying those groups step by step.
+the benchmark uses (fused append and decode) and are checked on every KV
+group and every step, the oracle replaying the groups in parallel worker
+processes.
 """
 
 import math
@@ -16,7 +17,8 @@ from synth.streams import make_inputs, workload
 
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_harness import OUT_TOL, check_groups, run_gpu, say  # noqa: E402
+from tests.gpu_harness import (OUT_TOL, check_groups, check_groups_parallel, run_gpu,  # noqa: E402
+                               say)
 
 
 def all_groups(w):
@@ -95,7 +97,8 @@ def test_merge_over_many_slices(max_slices):
 
 @pytest.mark.parametrize("fused,page_size,capacity", [(False, 0, 30000), (True, 0, 30000),
                                                        (False, 16, 30000), (True, 16, 30000),
-                                                       (True, 0, 70000), (False, 16, 70000)])
+                                                       (True, 0, 70000), (False, 16, 70000),
+                                                       (True, 16, 70000)])
 def test_two_rounds_every_step(fused, page_size, capacity):
     # a capacity far above the contexts gives the default launch more
     # rounds of workgroups (4 slices per group in the first round; 8 slices
@@ -244,30 +247,47 @@ def test_nan_query_poisons_only_its_head():
 
 
 # ---------------------------------------------------------------------------
-# full sizes, launch configuration of the benchmark, sampled groups
+# full sizes, launch configuration of the benchmark, every KV group and step
 # ---------------------------------------------------------------------------
 
 FULL = {
-    "8b_32k": (dict(), None, [(0, 0), (0, 5)]),
-    "8b_128k_p02": (dict(p_jump=0.2), 96, [(0, 3)]),
-    "paged_b8": (dict(), 64, [(2, 1), (7, 6)]),
-    "70b_128k": (dict(), 40, [(1, 2)]),
-    "8b_128k_mqa": (dict(n_kv_heads=1, p_jump=0.2), 24, [(0, 0)]),
+    # name: (workload, overrides, decode steps)
+    "8b_32k": ("8b_32k", dict(), 256),
+    "8b_128k_p1": ("8b_128k", dict(p_jump=1.0), 512),
+    "8b_128k_p05": ("8b_128k", dict(p_jump=0.5), 512),
+    "8b_128k_p02": ("8b_128k", dict(p_jump=0.2), 512),
+    "8b_128k_p005": ("8b_128k", dict(p_jump=0.05), 512),
+    "paged_b8": ("paged_b8", dict(), 128),
+    "70b_128k": ("70b_128k", dict(), 256),
+    # the labelled supplement: rho drawn per KV head (shared by its 8 query
+    # heads), so that whole groups hit and take the band-and-tail path
+    "70b_128k_rho_per_kv": ("70b_128k", dict(rho_per_kv=True), 256),
+    "8b_128k_mqa": ("8b_128k", dict(n_kv_heads=1, p_jump=0.2), 48),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled_groups(name):
-    kw, steps, groups = FULL[name]
-    base = name.split("_p0")[0].replace("_mqa", "")
-    w = workload(base, **kw)
-    say(f"[full:{name}] generating")
-    inp = make_inputs(w, steps=steps)
-    say(f"[full:{name}] gpu run")
-    gpu = run_gpu(w, inp)
-    say(f"[full:{name}] oracle replay of {groups}")
-    rep = check_groups(w, inp, gpu, groups)
-    assert_report(rep, f"full:{name}")
+def test_full_size_every_group(name):
+    base, kw, steps = FULL[name]
+    w = workload(base, **kw, steps=steps)
+    say(f"[full:{name}] generating {w}")
+    inp = make_inputs(w)
+    say(f"[full:{name}] gpu run, {steps} steps")
+    gpu = run_gpu(w, inp, fused=True)
+    groups = all_groups(w)
+    say(f"[full:{name}] oracle replay of {len(groups)} KV groups x {steps} steps")
+
+    def progress(i, n, rep):
+        if i == n or i % max(1, n // 8) == 0:
+            say(f"[full:{name}]   {i}/{n} groups, max_err {rep.max_err:.2e}, "
+                f"mismatches {len(rep.mismatches)}")
+
+    rep = check_groups_parallel(w, inp, gpu, groups, progress=progress)
+    assert rep.groups == len(groups) and rep.steps == len(groups) * steps
+    hit_rate = rep.hits / rep.heads
+    say(f"[full:{name}] head hit rate {hit_rate:.3f}, borderline decisions {len(rep.borderline)}")
+    # (every token jumps at p = 1: no step can hit)
+    assert_report(rep, f"full:{name}", min_hits=0 if w.p_jump >= 1.0 else 1)
 
 
 # ---------------------------------------------------------------------------
