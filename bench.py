@@ -8,28 +8,37 @@ tau = 0.5 sqrt(128)).  One step is one pass of the whole hot path for one
 token: append k/v, then match -> split-K attention -> merge (one attention
 layer).  L layer copies (own caches, rings and streams) are visited in turn
 so that consecutive steps do not find the previous step's KV in the 256 MB
-last-level cache.
+last-level cache.  Every layer copy's ring is seeded with the queries of
+the last W prefill positions before the first step, and the jumps of the
+query stream (a redrawn query, so a miss) fall on evenly spaced tokens at
+the point's rate: the timed steps hold exactly the jump rate's share of
+misses whatever their number.
 
 Printed: one JSON line.  `value` is the effective KV bandwidth of the miss
 path (every step misses: jump probability 1), i.e. algorithmic bytes / time;
 `sweep` holds the hit-rate sweep (jump probability 1, 0.5, 0.2, 0.05) with
-us/token, effective and dense-equivalent GB/s; `flatness` the hit-step
-latency at contexts 8K..128K; `latency_classes` per-step p10/p50/p90 at
-jump probability 0.2 split by the step's decisions (every head hit, every
-head missed, mixed); `seeding` the cost of seeding the rings from the
-prefill (1 and W positions); `drift` the largest |out_MAC - out_dense| on a
-16K continuous-generation stream by reuse-chain depth, over tau and B;
-`multilayer` every layer of a token in one graph (32 layers, 16K keys);
-`mqa` 32 query heads over one KV head at 128K keys;
-`read_ceiling` the rate of a plain streaming-read
-kernel on the same device; `roofline` the step kernel's achieved bandwidth
-from HIP events around its launches; `cpu_baseline` the fp64 oracle timed
-on a bounded sample of the same workload on the host cores.
+us/token, effective and dense-equivalent GB/s and the measured hit rates;
+`flatness` the hit-step latency at contexts 8K..128K; `latency_classes`
+per-step p10/p50/p90 at jump probability 0.2 split by the step's decisions
+(every head hit, every head missed, mixed); `configs` the other workloads
+(8B shape at 32K keys, the ragged paged batch of 8, the 70B shape and its
+rho-per-KV-head supplement): miss path with the step kernel's achieved
+bandwidth, the workload's own stream and the all-hit step; `seeding` the
+cost of seeding the rings from the prefill (1 and W positions); `drift` the
+largest |out_MAC - out_dense| on a 16K continuous-generation stream by
+reuse-chain depth, over tau and B; `multilayer` every layer of a token in
+one graph (32 layers, 16K keys); `mqa` 32 query heads over one KV head at
+128K keys; `read_ceiling` the rate of a plain streaming-read kernel on the
+same device; `roofline` the step kernel's achieved bandwidth from HIP events
+around its launches; `cpu_baseline` the fp64 oracle timed on a bounded
+sample of the same workload on the host cores, with per-class and
+single-thread figures on the 8B 32K stream.
 """
 
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
 import math
@@ -141,31 +150,72 @@ class Layer:
         self.t += 1
 
 
-def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefill_upto=None):
+def layer_inputs(w, p_jump, per_layer, layer, inputs_cache, seed_hist=0, jumps=None):
+    """Inputs of one layer copy: the workload's draws for `per_layer` decode
+    steps (keys and values cached per (workload, layer, per_layer)), with a
+    query stream of seed_hist + per_layer tokens whose first seed_hist are
+    the last prefill positions (seeded into the ring before decoding).
+    `jumps` [per_layer] bool: an explicit jump schedule for the decode
+    tokens (none in the seeded history)."""
     from synth.streams import make_inputs, make_q_stream
+    key = (w.name, w.batch, w.n_kv_heads, layer, per_layer)
+    if inputs_cache is not None and key in inputs_cache:
+        base = inputs_cache[key]
+    else:
+        base = make_inputs(w, p_jump=p_jump, layer=layer, steps=per_layer)
+        if inputs_cache is not None:
+            inputs_cache[key] = base
+    sched = None
+    if jumps is not None:
+        sched = np.concatenate([np.zeros(seed_hist, bool), np.asarray(jumps, bool)])
+    q, q64 = make_q_stream(w, p_jump=p_jump, layer=layer, steps=seed_hist + per_layer,
+                           jumps=sched)
+    inp = base.__class__(**{**base.__dict__, "q": q[seed_hist:], "q64": q64[seed_hist:]})
+    return inp, (q[:seed_hist] if seed_hist else None)
+
+
+def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefill_upto=None,
+                seed_hist=0, jumps=None):
+    """`layers` layer copies, prefilled (and, with seed_hist > 0, their rings
+    seeded with the queries of the last seed_hist prefill positions).
+    jumps: [layers][per_layer] bool schedules, or None for Bernoulli(p)."""
+    import torch
     Ls = []
     for l in range(layers):
-        key = (w.name, l, per_layer)
-        if inputs_cache is not None and key in inputs_cache:
-            base = inputs_cache[key]
-            q, q64 = make_q_stream(w, p_jump=p_jump, layer=l, steps=per_layer)
-            inp = base.__class__(**{**base.__dict__, "q": q, "q64": q64})
-        else:
-            inp = make_inputs(w, p_jump=p_jump, layer=l, steps=per_layer)
-            if inputs_cache is not None:
-                inputs_cache[key] = inp
+        inp, hist = layer_inputs(w, p_jump, per_layer, l, inputs_cache, seed_hist,
+                                 None if jumps is None else jumps[l])
         if prefill_upto is not None:
-            inp = inp.__class__(**{**inp.__dict__,
-                                   "contexts": np.full(w.batch, prefill_upto)})
+            inp = inp.__class__(**{**inp.__dict__, "contexts": np.full(w.batch, prefill_upto)})
         mc = int(inp.contexts.max()) + per_layer if context is None else context
-        Ls.append(Layer(w, inp, per_layer, max_context=mc))
+        L = Layer(w, inp, per_layer, max_context=mc)
+        L.hist = hist
+        Ls.append(L)
     for L in Ls:
         L.prefill()
+        if L.hist is not None:
+            L.sess.seed(L.hist.to(torch.device("cuda")).contiguous())
     return Ls
 
 
+def layer_jump_schedules(p, steps, warmup, layers, per_layer):
+    """Evenly spaced jumps at rate p over the timed steps (and, separately,
+    over the warm-up), dealt to the layer copies in the round-robin order the
+    steps visit them: the timed steps then hold floor or ceil of p * steps
+    jumps whatever their number."""
+    from synth.streams import even_jumps
+    J = np.concatenate([even_jumps(p, 0, warmup), even_jumps(p, 0, steps)])
+    out = []
+    for l in range(layers):
+        m = np.zeros(per_layer, bool)
+        mine = J[l::layers]
+        m[:len(mine)] = mine
+        out.append(m)
+    return out
+
+
 def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
-              context=None, prefill_upto=None, inputs_cache=None, per_step=False):
+              context=None, prefill_upto=None, inputs_cache=None, per_step=False,
+              seeded=False):
     """warmup + steps decode steps, round-robin over `layers` layer copies.
 
     The warmup runs eagerly.  With `graph` the timed steps are captured into
@@ -174,11 +224,15 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     they are launched eagerly.  `kernel_timing` (eager only) brackets every
     split-K attention launch with HIP events on the step's stream.  With
     `per_step` (eager) every step is bracketed by events too and the
-    durations come back as the fifth value."""
+    durations come back as the fifth value.  `seeded`: every layer's ring is
+    seeded with W prefill queries and the jumps follow the evenly spaced
+    schedule (so that a short run sees the jump rate p exactly)."""
     import torch
     from kv_cache_reuse_amd import binding as B
     per_layer = (steps + warmup + layers - 1) // layers + 1
-    Ls = make_layers(w, p_jump, per_layer, layers, inputs_cache, context, prefill_upto)
+    jumps = layer_jump_schedules(p_jump, steps, warmup, layers, per_layer) if seeded else None
+    Ls = make_layers(w, p_jump, per_layer, layers, inputs_cache, context, prefill_upto,
+                     seed_hist=w.window if seeded else 0, jumps=jumps)
     torch.cuda.synchronize()
     order = [i % layers for i in range(warmup + steps)]
     for i in order[:warmup]:
@@ -228,12 +282,13 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
             B.mac_profile_enable(L.sess.ctx, False)
     recs = []
     mns = []
+    hist = w.window if seeded else 0
     for li, L in enumerate(Ls):
         mn = L.match_n[:L.t].cpu().numpy()
         mns.append(mn)
         for t in range(starts[li], L.t):
             n_ctx = L.inp.contexts + t + 1
-            cnt = np.full((w.batch, w.n_q_heads), min(t, w.window))
+            cnt = np.full((w.batch, w.n_q_heads), min(t + hist, w.window))
             recs.append((n_ctx, mn[t], cnt))
     classes = [(("all_hit" if (mns[i][t] >= 0).all() else
                  "all_miss" if (mns[i][t] < 0).all() else "mixed"), us)
@@ -248,11 +303,11 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     return ms, recs, kms, klaunch
 
 
-def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache):
+def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache, seeded=False):
     """Per-step latency (HIP events around each eager step) by the step's
     decisions: every head hit, every head missed, or mixed."""
     out = run_point(w, p_jump, steps, warmup, layers, graph=False, inputs_cache=inputs_cache,
-                    per_step=True)
+                    per_step=True, seeded=seeded)
     res = {}
     for cls in ("all_hit", "mixed", "all_miss"):
         v = np.array([us for c, us in out[4] if c == cls])
@@ -402,7 +457,8 @@ def multilayer(layers=32, tokens=32):
     cache = {}
     for p in (0.05, 1.0):
         steps = layers * tokens
-        ms, recs, _, _ = run_point(w, p, steps, layers * 2, layers, inputs_cache=cache)
+        ms, recs, _, _ = run_point(w, p, steps, layers * 2, layers, inputs_cache=cache,
+                                   seeded=True)
         st = summarize(w, ms, recs, steps)
         out.append({"p_jump": p, "layers": layers, "tokens": tokens,
                     "us_per_token_all_layers": 1e3 * ms / tokens,
@@ -426,7 +482,7 @@ def mqa(steps, warmup, cache=None):
     _, _, kms, kl = run_point(w, 1.0, steps, warmup, 2, kernel_timing=True,
                               inputs_cache=cache)
     kbytes = 131073 * 2 * w.head_dim * w.bytes_per_elem
-    msh, rh, _, _ = run_point(w, 0.0, steps, warmup, 2, inputs_cache=cache)
+    msh, rh, _, _ = run_point(w, 0.0, steps, warmup, 2, inputs_cache=cache, seeded=True)
     sh = summarize(w, msh, rh, steps)
     res = {"workload": "8b_128k with 1 KV head: 32 query heads in 2 chunks of 16",
            "miss_us_per_step": st["us_per_step"], "miss_kernel_us": 1e3 * kms / max(kl, 1),
@@ -437,37 +493,64 @@ def mqa(steps, warmup, cache=None):
     return res
 
 
-def batch_point(steps, warmup, cache=None):
-    """A ragged batch on a paged cache: 8 sequences of 16K-64K keys (32 query
-    / 8 KV heads, d 128, bf16 K/V, 16-token pages).  Miss path: graph-replayed
-    steps, and the step kernel timed by HIP events in an eager run; then the
-    graph-replayed step at jump probability 0.1 and 0."""
+CONFIG_POINTS = {
+    # key: (workload, overrides, layer copies visited in turn, description)
+    "8b_32k": ("8b_32k", {}, 4,
+               "8b_32k: batch 1, 32 query / 8 KV heads, d 128, bf16 K/V, 32768-key context, "
+               "W 32, B 256, tau calibrated to 80 % head hits, jump probability 0.1"),
+    "paged_b8": ("paged_b8", {}, 2,
+                 "paged_b8: batch 8, contexts 16K-64K keys (ragged), 32 query / 8 KV heads, "
+                 "d 128, bf16 K/V, paged cache (16-token pages), W 32, B 128, jump probability 0.1"),
+    "70b_128k": ("70b_128k", {}, 1,
+                 "70b_128k: batch 4, 64 query / 8 KV heads (G 8), d 128, bf16 K/V with 1 % "
+                 "outlier keys x8, 131072-key context, W 64, B 256, rho U[0.8, 0.99] per query "
+                 "head, jump probability 0.1"),
+    "70b_128k_rho_per_kv": ("70b_128k", dict(rho_per_kv=True), 1,
+                            "70b_128k with rho drawn per KV head (shared by its 8 query heads)"),
+}
+
+
+def config_point(key, steps, warmup, cache, miss=True, classes=False):
+    """One workload of the configs: its miss path (every token jumps), graph-
+    replayed, with the step kernel timed by HIP events in an eager run (that
+    kernel's roofline at this shape); its own query stream (its jump
+    probability as an evenly spaced schedule, rings seeded with W prefill
+    queries); and the step when every head hits (no jumps)."""
     from synth.streams import workload
-    w = workload("paged_b8", p_jump=1.0)
-    ms, recs, _, _ = run_point(w, 1.0, steps, warmup, 2, inputs_cache=cache)
-    st = summarize(w, ms, recs, steps)
-    _, recs_k, kms, kl = run_point(w, 1.0, steps, warmup, 2, kernel_timing=True,
-                                   inputs_cache=cache)
-    keys = sum(step_bytes(w, *r)[2] for r in recs_k)
-    kbytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(kl, 1)
-    kus = 1e3 * kms / max(kl, 1)
-    res = {"workload": "paged_b8: batch 8, contexts 16K-64K keys (ragged), 32 query / 8 KV heads, "
-                       "d 128, bf16 K/V, paged cache (16-token pages), miss path",
-           "us_per_step": st["us_per_step"], "eff_GBps": st["eff_GBps"],
-           "kernel_us": kus, "kernel_GBps": kbytes / kus / 1e3,
-           "kernel_pct_hbm_peak": 100.0 * kbytes / kus / 1e3 / HBM_PEAK_GBPS}
-    log(f"  batch: {res['us_per_step']:.1f} us/step, step kernel {kus:.1f} us "
-        f"({res['kernel_GBps']:.0f} GB/s of KV)")
-    # the same batch at the stream's own jump rate and with no jumps
-    res["mixed"] = []
-    for p in (0.1, 0.0):
-        wp = workload("paged_b8", p_jump=p)
-        msp, rp, _, _ = run_point(wp, p, steps, warmup, 2, inputs_cache=cache)
-        sp = summarize(wp, msp, rp, steps)
-        res["mixed"].append({"p_jump": p, "us_per_step": sp["us_per_step"],
-                             "hit_rate": sp["hit_rate"], "group_all_hit": sp["group_all_hit"]})
-        log(f"  batch p={p}: {sp['us_per_step']:.1f} us/step (hit {sp['hit_rate']:.2f}, "
-            f"group all-hit {sp['group_all_hit']:.2f})")
+    name, kw, layers, desc = CONFIG_POINTS[key]
+    w = workload(name, **kw)
+    res = {"workload": desc, "layers_rotated": layers}
+    if miss:
+        ms, recs, _, _ = run_point(w, 1.0, steps, warmup, layers, inputs_cache=cache, seeded=True)
+        st = summarize(w, ms, recs, steps)
+        _, recs_k, kms, kl = run_point(w, 1.0, steps, warmup, layers, kernel_timing=True,
+                                       inputs_cache=cache, seeded=True)
+        keys = sum(step_bytes(w, *r)[2] for r in recs_k)
+        kbytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(kl, 1)
+        kus = 1e3 * kms / max(kl, 1)
+        res["miss"] = {"us_per_step": st["us_per_step"], "eff_GBps": st["eff_GBps"],
+                       "pct_hbm_peak": st["pct_hbm_peak"], "kernel_us": kus,
+                       "kernel_bytes_per_launch": kbytes, "kernel_GBps": kbytes / kus / 1e3,
+                       "kernel_frac_hbm_peak": kbytes / kus / 1e3 / HBM_PEAK_GBPS,
+                       "launches": kl}
+        log(f"  {key} miss: {st['us_per_step']:.1f} us/step ({st['eff_GBps']:.0f} GB/s), step "
+            f"kernel {kus:.1f} us = {kbytes / kus / 1e3:.0f} GB/s "
+            f"({100 * kbytes / kus / 1e3 / HBM_PEAK_GBPS:.1f} % of 8 TB/s)")
+    for label, p in (("stream", w.p_jump), ("all_hit", 0.0)):
+        msp, rp, _, _ = run_point(w, p, steps, warmup, layers, inputs_cache=cache, seeded=True)
+        sp = summarize(w, msp, rp, steps)
+        res[label] = {"p_jump": p, "us_per_step": sp["us_per_step"],
+                      "us_per_token": sp["us_per_token"], "eff_GBps": sp["eff_GBps"],
+                      "dense_equiv_GBps": sp["dense_equiv_GBps"], "hit_rate": sp["hit_rate"],
+                      "group_all_hit": sp["group_all_hit"]}
+        log(f"  {key} p={p}: {sp['us_per_step']:.1f} us/step (hit {sp['hit_rate']:.3f}, group "
+            f"all-hit {sp['group_all_hit']:.3f}, dense-equivalent {sp['dense_equiv_GBps']:.0f} GB/s)")
+    if classes:
+        res["latency_classes"] = latency_classes(w, w.p_jump, steps, warmup, layers, cache,
+                                                 seeded=True)
+        for k, v in res["latency_classes"].items():
+            log(f"  {key} {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / "
+                f"{v['p50_us']:.1f} / {v['p90_us']:.1f} us")
     return res
 
 
@@ -568,6 +651,66 @@ def cpu_baseline(w, sample_steps):
     }
 
 
+def cpu_classes(sample_steps, single_steps):
+    """The oracle per decision class on the 8b_32k stream, whose calibrated
+    tau makes steps where every head hits, some heads hit and every head
+    misses all occur.  Rings seeded with W prefill queries (untimed, the
+    oracle's own seeding).  Each step timed alone: us/step and algorithmic
+    GB/s per class on all host threads, and the mean of a shorter sample on
+    one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import mac_oracle as M
+    from synth.streams import make_inputs, make_q_stream, workload
+    w = workload("8b_32k")
+    W = w.window
+    cores = len(os.sched_getaffinity(0))
+    T = max(sample_steps, single_steps)
+    inp = make_inputs(w, steps=T)
+    _, q64 = make_q_stream(w, steps=W + T)
+    K = inp.k.float().numpy()
+    V = inp.v.float().numpy()
+    n0 = int(inp.contexts[0])
+
+    seeded = M.MacOracle.for_workload(w)
+    with threadpool_limits(limits=cores):
+        seeded.seed(0, q64[:W, 0], K[0], V[0], n0)
+
+    def run(steps, threads):
+        orc = copy.deepcopy(seeded)
+        out = []
+        with threadpool_limits(limits=threads):
+            used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            for t in range(steps):
+                n = n0 + t + 1
+                t0 = time.perf_counter()
+                r = orc.step(0, q64[W + t, 0], K[0], V[0], n)
+                sec = time.perf_counter() - t0
+                mn = r.match_n.reshape(1, -1).astype(np.int64)
+                b = step_bytes(w, np.array([n]), mn, np.full((1, w.n_q_heads), W))[0]
+                cls = "all_hit" if r.hit.all() else "all_miss" if not r.hit.any() else "mixed"
+                out.append((cls, sec, b))
+        return out, used
+
+    rows, used = run(sample_steps, cores)
+    per = {}
+    for cls in ("all_hit", "mixed", "all_miss"):
+        sel = [(sec, b) for c, sec, b in rows if c == cls]
+        if sel:
+            sec = sum(x for x, _ in sel)
+            per[cls] = {"steps": len(sel), "us_per_step": 1e6 * sec / len(sel),
+                        "GBps": sum(b for _, b in sel) / sec / 1e9}
+    one, used1 = run(single_steps, 1)
+    sec1 = sum(x for _, x, _ in one)
+    return {
+        "per_class": {"workload": "8b_32k stream (jump probability 0.1, tau for 80 % head "
+                                  "hits), rings seeded; each step timed alone",
+                      "threads": int(used), "classes": per},
+        "single_thread": {"workload": "8b_32k stream, the same steps", "threads": int(used1),
+                          "steps": single_steps, "us_per_step": 1e6 * sec1 / single_steps,
+                          "GBps": sum(b for _, _, b in one) / sec1 / 1e9},
+    }
+
+
 def kernel_sha256():
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
@@ -603,6 +746,8 @@ def main():
     ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--no-mqa", action="store_true")
     ap.add_argument("--no-batch", action="store_true")
+    ap.add_argument("--no-c2", action="store_true")
+    ap.add_argument("--no-c5", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -635,11 +780,11 @@ def main():
     # ---- headline: miss path (jump probability 1)
     log(f"headline: {w.name} p_jump=1 steps={args.steps} warmup={args.warmup} layers={args.layers}")
     ms, recs, _, _ = run_point(w, 1.0, args.steps, args.warmup, args.layers,
-                               inputs_cache=cache)
+                               inputs_cache=cache, seeded=True)
     head = summarize(w, ms, recs, args.steps)
     log(f"headline (graph): {head['us_per_token']:.1f} us/token, {head['eff_GBps']:.0f} GB/s")
     ms_e, recs_e, _, _ = run_point(w, 1.0, args.steps, args.warmup, args.layers, graph=False,
-                                   inputs_cache=cache)
+                                   inputs_cache=cache, seeded=True)
     head_eager = summarize(w, ms_e, recs_e, args.steps)
     log(f"headline (eager): {head_eager['us_per_token']:.1f} us/token, "
         f"{head_eager['eff_GBps']:.0f} GB/s")
@@ -647,7 +792,7 @@ def main():
     # ---- step kernel timing (HIP events around each launch, on its stream)
     log("kernel timing pass")
     ms_k, recs_k, kms, klaunch = run_point(w, 1.0, args.steps, args.warmup, args.layers,
-                                           kernel_timing=True, inputs_cache=cache)
+                                           kernel_timing=True, inputs_cache=cache, seeded=True)
     keys = sum(step_bytes(w, *r)[2] for r in recs_k)
     kern_bytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(klaunch, 1)
     kern_sec = kms / 1e3 / max(klaunch, 1)
@@ -669,10 +814,10 @@ def main():
             else:
                 log(f"sweep point p_jump={p}")
                 msp, rp, _, _ = run_point(w, p, args.steps, args.warmup, args.layers,
-                                          inputs_cache=cache)
+                                          inputs_cache=cache, seeded=True)
                 s = summarize(w, msp, rp, args.steps)
                 mse, re_, _, _ = run_point(w, p, args.steps, args.warmup, args.layers,
-                                           graph=False, inputs_cache=cache)
+                                           graph=False, inputs_cache=cache, seeded=True)
                 s["us_per_token_eager"] = summarize(w, mse, re_, args.steps)["us_per_token"]
             if p == 1.0:
                 s["us_per_token_eager"] = head_eager["us_per_token"]
@@ -690,7 +835,7 @@ def main():
     lat = None
     if not args.no_latency:
         log("latency classes: p_jump=0.2, eager per-step events")
-        lat = latency_classes(w, 0.2, args.steps, args.warmup, args.layers, cache)
+        lat = latency_classes(w, 0.2, args.steps, args.warmup, args.layers, cache, seeded=True)
         for k, v in lat.items():
             log(f"  {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / {v['p50_us']:.1f} / "
                 f"{v['p90_us']:.1f} us")
@@ -713,11 +858,18 @@ def main():
         log("multi-layer graph: gen_16k shape, 32 layers")
         multi = multilayer()
 
-    # ---- a ragged batch on a paged cache
-    bt = None
-    if not args.no_batch:
-        log("batch: 8 ragged sequences (16K-64K keys), paged cache")
-        bt = batch_point(min(args.steps, 64), min(args.warmup, 8), {})
+    # ---- the other configs: 8B at 32K, the ragged paged batch, the 70B shape
+    configs = {}
+    cfg_keys = [k for k in CONFIG_POINTS
+                if not (k == "8b_32k" and args.no_c2) and not (k == "paged_b8" and args.no_batch)
+                and not (k.startswith("70b") and args.no_c5)]
+    for key in cfg_keys:
+        log(f"config point {key}")
+        configs[key] = config_point(key, min(args.steps, 64), min(args.warmup, 8),
+                                    cache if key != "paged_b8" else {},
+                                    miss=key != "70b_128k_rho_per_kv", classes=key == "8b_32k")
+        if key.startswith("70b"):
+            cache = {k: v for k, v in cache.items() if not k[0].startswith("70b")}
 
     # ---- MQA / groups wider than the 16-head tile
     mq = None
@@ -738,6 +890,10 @@ def main():
         log(f"cpu baseline: oracle, {args.cpu_steps} steps")
         cpu = cpu_baseline(w, args.cpu_steps)
         log(f"cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+        cpu.update(cpu_classes(48, 12))
+        for k, v in cpu["per_class"]["classes"].items():
+            log(f"  oracle {k}: {v['steps']} steps, {v['us_per_step']:.0f} us/step")
+        log(f"  oracle on one thread: {cpu['single_thread']['us_per_step']:.0f} us/step")
 
     line = {
         "metric": METRIC,
@@ -768,7 +924,7 @@ def main():
         "drift": drift,
         "multilayer": multi,
         "mqa": mq,
-        "batch": bt,
+        "configs": configs,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,

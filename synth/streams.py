@@ -172,13 +172,22 @@ def rho_per_head(w: Workload, layer: int = 0) -> np.ndarray:
     return rng.uniform(lo, hi, size=w.n_q_heads)
 
 
+def even_jumps(p: float, start: int, count: int) -> np.ndarray:
+    """A jump schedule at rate p with the jumps evenly spaced: token i jumps
+    iff floor((i + 1) p) > floor(i p), for i in [start, start + count).  Any
+    run of n consecutive tokens then holds floor(n p) or ceil(n p) jumps."""
+    i = np.arange(start, start + count, dtype=np.float64)
+    return np.floor((i + 1) * p) > np.floor(i * p)
+
+
 def make_q_stream(w: Workload, p_jump: Optional[float] = None, layer: int = 0,
-                  steps: Optional[int] = None):
+                  steps: Optional[int] = None, jumps: Optional[np.ndarray] = None):
     """Pre-RoPE query stream.
 
     Returns ``(q, q64)``: ``q`` is a CPU tensor ``[T, batch, Hq, d]`` in the
     workload dtype and ``q64`` the float64 numpy copy of the same rounded
-    values.
+    values.  ``jumps`` ([T] or [T, batch] bool) replaces the Bernoulli(p)
+    jump draws by a given schedule.
     """
     p = w.p_jump if p_jump is None else p_jump
     T = w.steps if steps is None else steps
@@ -186,13 +195,17 @@ def make_q_stream(w: Workload, p_jump: Optional[float] = None, layer: int = 0,
     eps = np.random.default_rng(ch["q"]).standard_normal(
         (T, w.batch, w.n_q_heads, w.head_dim))
     u = np.random.default_rng(ch["jump"]).random((T, w.batch))
+    if jumps is None:
+        jump_at = u < p
+    else:
+        jump_at = np.broadcast_to(np.asarray(jumps, dtype=bool).reshape(T, -1), (T, w.batch))
     rho = rho_per_head(w, layer)[None, :, None]
     c = np.sqrt(1.0 - rho * rho)
     q = np.empty_like(eps)
     q[0] = eps[0]
     for t in range(1, T):
         ar = rho * q[t - 1] + c * eps[t]
-        jump = (u[t] < p)[:, None, None]
+        jump = jump_at[t][:, None, None]
         q[t] = np.where(jump, eps[t], ar)
     if w.period > 0:
         for t in range(w.period, T):
