@@ -754,6 +754,8 @@ def main():
     ap.add_argument("--points", type=str, default="")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 512 MiB device-to-device (counter calibration)")
+    ap.add_argument("--config-only", type=str, default="",
+                    help="run only this config point (for profiling its kernels) and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step "
@@ -776,6 +778,17 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {COPY_CAL_BYTES} bytes read and written")
         del src, dst
+
+    if args.config_only:
+        key = args.config_only
+        if key not in CONFIG_POINTS:
+            print(f"unknown config point {key}; one of {sorted(CONFIG_POINTS)}", file=sys.stderr)
+            sys.exit(2)
+        log(f"config point {key} only")
+        res = config_point(key, args.steps, args.warmup, cache,
+                           miss=key != "70b_128k_rho_per_kv")
+        print(json.dumps({"config_only": key, **res}), flush=True)
+        return
 
     # ---- headline: miss path (jump probability 1)
     log(f"headline: {w.name} p_jump=1 steps={args.steps} warmup={args.warmup} layers={args.layers}")

@@ -85,11 +85,19 @@ struct Layout {
 
 int elem_size(int dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
 
-// A KV head with G > kMaxGroup query heads is processed as nchunk groups of
-// G / nchunk heads (the matrix-core tile is 16 heads wide).
+// Wide groups: bf16 caches with G > kMaxGroup query heads per KV head.  They
+// are matched in a launch of their own and attended by workgroups of up to
+// kWideGroup heads (two matrix-core column tiles); fp32 caches keep 16-head
+// groups matched inside the attention workgroups.
+bool wide_mode(const mac_config* c) {
+  return c->dtype == MAC_DTYPE_BF16 && c->n_q_heads / c->n_kv_heads > mac::kMaxGroup;
+}
+// A KV head whose G query heads exceed one group is processed as nchunk
+// groups of G / nchunk heads ("virtual" KV heads reading the same cache).
+int chunk_cap(const mac_config* c) { return wide_mode(c) ? mac::kWideGroup : mac::kMaxGroup; }
 int n_chunks(const mac_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
-  return (G + mac::kMaxGroup - 1) / mac::kMaxGroup;
+  return (G + chunk_cap(c) - 1) / chunk_cap(c);
 }
 int chunk_heads(const mac_config* c) { return c->n_q_heads / c->n_kv_heads / n_chunks(c); }
 
@@ -102,17 +110,18 @@ mac_status check_config(const mac_config* c) {
   if (c->n_q_heads % c->n_kv_heads)
     return fail(MAC_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
                 c->n_q_heads, c->n_kv_heads);
-  {
-    const int G = c->n_q_heads / c->n_kv_heads;
-    const int nc = (G + mac::kMaxGroup - 1) / mac::kMaxGroup;
-    if (G % nc)
-      return fail(MAC_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d must split into "
-                  "%d equal groups of at most %d", G, mac::kMaxGroup, nc, mac::kMaxGroup);
-  }
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(MAC_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
   if (c->dtype != MAC_DTYPE_F32 && c->dtype != MAC_DTYPE_BF16)
     return fail(MAC_ERR_UNSUPPORTED, "dtype must be MAC_DTYPE_F32 or MAC_DTYPE_BF16 (got %d)", c->dtype);
+  {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    const int cap = chunk_cap(c);
+    const int nc = (G + cap - 1) / cap;
+    if (G % nc)
+      return fail(MAC_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d must split into "
+                  "%d equal groups of at most %d", G, cap, nc, cap);
+  }
   if (c->window < 0) return fail(MAC_ERR_INVALID_ARG, "window must be >= 0 (got %d)", c->window);
   if (c->band < 0) return fail(MAC_ERR_INVALID_ARG, "band must be >= 0 (got %d)", c->band);
   if (!(c->tau >= 0.f)) return fail(MAC_ERR_INVALID_ARG, "tau must be >= 0 (got %g)", (double)c->tau);
@@ -181,14 +190,17 @@ Layout layout(const mac_config* c) {
     if (S < 2) S = 2;
   }
   const size_t G = chunk_heads(c);
-  if (S * G > (size_t)mac::kMergeCap) S = mac::kMergeCap / (int)G;
+  const size_t merge_cap = wide_mode(c) ? mac::kMergeCapWide : mac::kMergeCap;
+  if (S * G > merge_cap) S = (int)(merge_cap / G);
   L.slices = S;
   if (L.first <= 0 || L.first > S) L.first = S;
   off = 0;
   L.w_po = off;      off = align256(off + (size_t)groups * S * G * d * 4);
   L.w_pml = off;     off = align256(off + (size_t)groups * S * G * 2 * 4);
   L.w_heads = off;   off = align256(off + bh * sizeof(mac::HeadState));
-  L.w_reuse = off;   off = align256(off + bh * (d + 2) * 4);   // o rows, then (m, l) pairs
+  // o rows, then (m, l) pairs, then (16-byte aligned) the wide path's
+  // rotated query rows (bf16 hi and lo per head)
+  L.w_reuse = off;   off = align256(off + bh * (d + 2) * 4 + 16 + bh * 2 * d * 2);
   L.w_out = off;   off = align256(off + bh * d * 4);          // ring seeding: discarded outputs
   L.w_save = off;  off = align256(off + (size_t)c->batch * 4); // ring seeding: saved lengths
   L.w_pub = off;   off = align256(off + (size_t)groups * 8);    // second round: published plans

@@ -15,6 +15,11 @@ constexpr int kSliceMin = 64;    // fewest keys a split-K slice is given (4 tile
 constexpr int kMaxSlices = 1024; // most split-K slices per KV group
 constexpr int kMaxGroup = 16;    // query heads per KV head: the MFMA N width
 constexpr int kMergeCap = 2048;  // most (query head, slice) pairs one merge holds
+// Wide groups (bf16 caches, more than kMaxGroup query heads per KV head) are
+// matched in a launch of their own and attended in groups of at most
+// kWideGroup heads, two matrix-core column tiles per key fragment.
+constexpr int kWideGroup = 32;
+constexpr int kMergeCapWide = 8192;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));

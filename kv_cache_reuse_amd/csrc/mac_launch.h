@@ -12,6 +12,12 @@ namespace mac {
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1);
 
+// Wide groups (bf16, more than kMaxGroup heads per group): the match of
+// every query head (records, rotated queries, reused states) and the split-K
+// attention that reads them (wide.hip).
+hipError_t launch_match_wide(const StepArgs& a, int d, hipStream_t st);
+hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st);
+
 hipError_t launch_append(void* kc, void* vc, const int32_t* pt, const void* kn, const void* vn,
                          int32_t* seq_lens, const KvGeom& geom, int batch, int dtype,
                          hipStream_t st);

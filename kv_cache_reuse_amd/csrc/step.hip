@@ -49,68 +49,9 @@
 
 #include "mac_dev.h"
 #include "mac_launch.h"
+#include "match.h"
 
 namespace mac {
-
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-
-constexpr double kLog2e = 1.4426950408889634074;
-constexpr float kLn2 = 0.69314718055994530942f;
-// ring slots per 16-lane group per round.  A wave that takes all of a head's
-// slots covers 36 per round (a window of 32, 33 slots, in one round); two
-// waves that split a head's slots (even / odd) cover 20 each, 40 together.
-constexpr int kMatchSlotsWhole = 9;
-constexpr int kMatchSlotsHalf = 5;
-
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-
-// Raw buffer descriptor over `bytes` bytes at p: no stride, 32-bit data
-// format (the word the gfx9 family takes for untyped buffer access).
-// Offsets past `bytes` read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
-// Sum over each 16-lane row of the wave, result in every lane of the row:
-// DPP row rotations (VALU, no LDS round trip) by 8, 4, 2, 1.
-template <int N>
-__device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += row_ror<8>(v);
-  v += row_ror<4>(v);
-  v += row_ror<2>(v);
-  v += row_ror<1>(v);
-  return v;
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, row_ror<8>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  v = fmaxf(v, row_ror<1>(v));
-  return v;
-}
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-// Wave-wide max and sum, the same value in every lane: DPP within each row
-// of 16 lanes, then the four rows' results read from lanes 0, 16, 32, 48 in
-// a fixed order (no LDS round trip).
-__device__ __forceinline__ float wave_max(float v) {
-  v = row16_max(v);
-  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
-
-// Row stride of the query rows in LDS: four elements of padding, so that the
-// 16 head columns of a fragment read fall in different banks.
-__host__ __device__ constexpr int qstride(int d) { return d + 4; }
 
 template <int D, int NE, int OC>
 struct Shared {
@@ -129,233 +70,6 @@ struct Shared {
   __attribute__((aligned(16))) unsigned char patch[2 * D * 4];
   int leave;   // second round: the workgroup's slice is empty
 };
-
-// =========================================================== phase A ====
-// A wave matches one query head h (index hi in the group) over the ring
-// slots off, off + st, off + 2 st, ... (st = 2 splits a head's slots between
-// two waves).  The loads do not depend on the sequence length, so they are
-// issued first (match_load) and the length is read while they are in
-// flight; match_best then picks the best ring entry.  16 lanes share one
-// ring slot, each lane holding D/16 elements of the row; a round covers
-// 4 KMS slots.
-template <typename T, int D, int KMS>
-struct MatchIn {
-  static constexpr int EPL = D / 16;                       // elements per lane
-  static constexpr int NW = EPL * (int)sizeof(T) / 4;      // dwords per lane
-  uint32_t qw[NW];                          // this lane's piece of q_pre
-  uint32_t rw[KMS][NW];                     // its piece of the round's ring rows
-  int2 pnl;                                 // (p, n) of the round's slot `lane`
-  double inv;                               // theta^(-2 lane / D)
-  // rotate-half pair of this lane, widened to 32 bits: two 16-bit values
-  // sharing a register would have to be packed, which waits for both loads
-  uint32_t q1, q2;
-  int cnt;                                  // ring pushes so far
-};
-
-__device__ __forceinline__ uint32_t bits_of(uint16_t x) { return x; }
-__device__ __forceinline__ uint32_t bits_of(float x) { return __float_as_uint(x); }
-template <typename T> __device__ __forceinline__ float from_bits(uint32_t w);
-template <> __device__ __forceinline__ float from_bits<uint16_t>(uint32_t w) { return __uint_as_float(w << 16); }
-template <> __device__ __forceinline__ float from_bits<float>(uint32_t w) { return __uint_as_float(w); }
-
-// a lane's D/16 elements of one row as 2, 4 or 8 dwords, one vector load
-// (rows start 16-byte aligned, so the lane's piece is aligned too)
-template <typename T, int D>
-__device__ __forceinline__ void load_row(const T* src, uint32_t (&w)[D / 16 * (int)sizeof(T) / 4]) {
-  constexpr int NW = D / 16 * (int)sizeof(T) / 4;
-  if constexpr (NW == 2) {
-    const u2 v = *reinterpret_cast<const u2*>(src);
-    w[0] = v.x; w[1] = v.y;
-  } else if constexpr (NW == 4) {
-    const u4 v = *reinterpret_cast<const u4*>(src);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-    const u4 v0 = reinterpret_cast<const u4*>(src)[0];
-    const u4 v1 = reinterpret_cast<const u4*>(src)[1];
-    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-  }
-}
-
-// Ring slots s0 + st (gi + 4u) + off (u < KMS) of head bh, and the (p, n) of
-// slot s0 + st lane + off, one lane per slot.  Slot indices are clamped into
-// the ring; slots past W + 1 are dropped by the candidate test.
-template <typename T, int D, int KMS>
-__device__ __forceinline__ void load_slots(const StepArgs& a, int bh, int lane, int s0, int st,
-                                           int off, MatchIn<T, D, KMS>& mi) {
-  const RingView& R = a.ring;
-  const int gi = lane / 16, c = lane % 16;
-  const T* rq = static_cast<const T*>(R.q) + (size_t)bh * R.slots * D;
-  const int2* rpn = reinterpret_cast<const int2*>(R.pn) + (size_t)bh * R.slots;
-  // (p, n) first: loads complete in order, and the candidate mask needs them
-  const int sl = s0 + st * lane + off;
-  mi.pnl = rpn[sl < R.slots ? sl : 0];
-#pragma unroll
-  for (int u = 0; u < KMS; ++u) {
-    const int s = s0 + st * (gi + 4 * u) + off;
-    const int sc = s < R.slots ? s : 0;
-    load_row<T, D>(rq + (size_t)sc * D + c * MatchIn<T, D, KMS>::EPL, mi.rw[u]);
-  }
-}
-
-template <typename T, int D, int KMS>
-__device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, int st, int off,
-                                           MatchIn<T, D, KMS>& mi) {
-  const T* q = static_cast<const T*>(a.q_pre) + (size_t)bh * D;
-  const bool rot = lane < D / 2;
-  mi.cnt = a.ring.count[bh];
-  mi.inv = rot ? a.inv_freq[lane] : 0.0;
-  mi.q1 = rot ? bits_of(q[lane]) : 0u;
-  mi.q2 = rot ? bits_of(q[lane + D / 2]) : 0u;
-  load_row<T, D>(q + (lane % 16) * MatchIn<T, D, KMS>::EPL, mi.qw);
-  load_slots<T, D, KMS>(a, bh, lane, 0, st, off, mi);
-}
-
-// Rotate-half pairs (i, i + D/2) of head hi's query: float64 angle and
-// rotation, result scaled by log2(e)/sqrt(D) so that the attention can use
-// exp2; pairs i0 <= i < i1 are stored in LDS as bf16 hi/lo halves (or fp32).
-// Every lane that loaded a pair computes it, so the loads are consumed.
-template <typename T, int D, int KMS, class SH>
-__device__ __forceinline__ void rope_q(SH& sh, int hi, int lane, int n, const MatchIn<T, D, KMS>& mi,
-                                       int i0 = 0, int i1 = D / 2) {
-  if (lane < D / 2) {
-    const int i = lane;
-    double sn, cs;
-    sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
-    const double x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
-    const double sc = kLog2e / sqrt(static_cast<double>(D));
-    const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
-    const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
-    if (i < i0 || i >= i1) return;
-    if constexpr (sizeof(T) == 2) {
-      uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * qstride(D);
-      uint16_t* ql = reinterpret_cast<uint16_t*>(sh.q) + (kMaxGroup + hi) * qstride(D);
-      const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
-      qh[i] = h1;
-      qh[i + D / 2] = h2;
-      ql[i] = f32_to_bf16(r1 - bf16_to_f32(h1));
-      ql[i + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
-    } else {
-      float* qs = reinterpret_cast<float*>(sh.q) + hi * qstride(D);
-      qs[i] = r1;
-      qs[i + D / 2] = r2;
-    }
-  }
-}
-
-// Best ring entry among this wave's slots: d2 = dist^2 (+inf if none),
-// k = its age (-1 if none), (p, n) of the entry.
-struct Best {
-  float d2;
-  int k, p, n;
-};
-
-// the better of two candidates: smaller distance, then the newer entry
-__device__ __forceinline__ bool better_than(float d2, int k, float bd2, int bk) {
-  return k >= 0 && (bk < 0 || d2 < bd2 || (d2 == bd2 && k < bk));
-}
-
-// Slot s holds the entry k = (cnt - 1 - s) mod (W + 1) steps old; it is a
-// candidate iff k < min(cnt, W) and 0 <= p <= p_new.  Best candidate:
-// smallest squared distance, then smallest k (the newest entry).  The
-// candidate test is taken one lane per slot and shared as a ballot mask; the
-// best entry's (p, n) come from the lane of its slot, so no load follows the
-// argmin.  Every wave consumes its loads (a wave past the group's heads
-// too): loads left unread make the compiler wait for every load in flight
-// before their registers are reused.
-template <typename T, int D, int KMS>
-__device__ __forceinline__ Best match_best(const StepArgs& a, int bh, int lane, int p_new, int st,
-                                           int off, MatchIn<T, D, KMS>& mi) {
-  constexpr int EPL = MatchIn<T, D, KMS>::EPL;
-  const int gi = lane / 16;
-  const RingView& R = a.ring;
-  auto elem = [&](const uint32_t (&w)[MatchIn<T, D, KMS>::NW], int e) -> float {
-    if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
-    else return __uint_as_float(w[e]);
-  };
-  const int cnt = mi.cnt;
-  const int nvalid = cnt < R.window ? cnt : R.window;
-  // slot s is (r - s) mod (W + 1) steps old, r = (cnt - 1) mod (W + 1)
-  const int r = cnt > 0 ? (cnt - 1) % R.slots : R.slots - 1;
-  float qv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = elem(mi.qw, e);
-  float best = __builtin_inff();
-  int bestk = -1, bp = 0, bn = -1;
-  auto age = [&](int s) { return s >= R.slots ? R.slots : (r >= s ? r - s : r - s + R.slots); };
-  auto round = [&](int s0) {
-    const int sl = s0 + st * lane + off;
-    const int pl = mi.pnl.x;
-    const bool cl = lane < 4 * KMS && age(sl) < nvalid && pl >= 0 && pl <= p_new;
-    const uint64_t cmask = __ballot(cl);
-    int bj = -1;   // this round's best slot (index within the round) in this lane
-#pragma unroll
-    for (int u = 0; u < KMS; ++u) {
-      if (s0 + st * 4 * u + off >= R.slots) break;   // the rest of the round is padding
-      const int j = gi + 4 * u;
-      float d2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float df = qv[e] - elem(mi.rw[u], e);
-        d2 = fmaf(df, df, d2);
-      }
-      d2 = row16_sum(d2);
-      const int k = age(s0 + st * j + off);
-      const bool cand = ((cmask >> j) & 1) != 0 && d2 == d2;
-      const bool better = cand && (d2 < best || (d2 == best && k < bestk));
-      best = better ? d2 : best;
-      bestk = better ? k : bestk;
-      bj = better ? j : bj;
-    }
-    const int px = __shfl(mi.pnl.x, bj >= 0 ? bj : 0, 64);
-    const int py = __shfl(mi.pnl.y, bj >= 0 ? bj : 0, 64);
-    bp = bj >= 0 ? px : bp;
-    bn = bj >= 0 ? py : bn;
-  };
-  // the first round straight-line: a loop header here would merge the
-  // pending-load state and wait for every load in flight, the first tile's
-  // included
-  // (the second round too; a loop takes the rest)
-  const int round_step = st * 4 * KMS;
-  round(0);
-  if (round_step + off < R.slots) {
-    load_slots<T, D, KMS>(a, bh, lane, round_step, st, off, mi);
-    round(round_step);
-  }
-  for (int s0 = 2 * round_step; s0 + off < R.slots; s0 += round_step) {
-    load_slots<T, D, KMS>(a, bh, lane, s0, st, off, mi);
-    round(s0);
-  }
-#pragma unroll
-  for (int xo = 16; xo <= 32; xo <<= 1) {
-    const float ob = shfl_xor_f(best, xo);
-    const int ok = shfl_xor_i(bestk, xo);
-    const int op = shfl_xor_i(bp, xo);
-    const int on = shfl_xor_i(bn, xo);
-    if (better_than(ob, ok, best, bestk)) {
-      best = ob;
-      bestk = ok;
-      bp = op;
-      bn = on;
-    }
-  }
-  return Best{best, bestk, bp, bn};
-}
-
-// The head's match record from its best entry.
-__device__ __forceinline__ HeadState head_record(const StepArgs& a, const Best& bst, int cnt, int n) {
-  const bool hit = bst.k >= 0 && bst.d2 < a.tau2;
-  HeadState hs;
-  hs.hit = hit ? 1 : 0;
-  hs.slot = hit ? (cnt - 1 - bst.k) % a.ring.slots : -1;
-  hs.s = hit ? bst.p : 0;
-  hs.cnt = cnt;
-  hs.match_n = hit ? bst.n : -1;
-  hs.dist = bst.k >= 0 ? sqrtf(bst.d2) : __builtin_inff();
-  hs.n = n;
-  hs.pad = 0;
-  return hs;
-}
 
 // ========================================================== the kernel ==
 // Waves per workgroup: 8, except for wide groups of fp32 d128 tiles, whose
@@ -935,6 +649,11 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   const int k1 = k0 + spw < S ? k0 + spw : S;           // empty when k0 >= S
 
   // ---- the loads
+  // the group's fresh-range starts, lane i < G holding head i's: one vector
+  // load, first (loads complete in order; a loop of scalar loads would wait
+  // for each record in turn)
+  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  const int s_lane = hsg[lane < G ? lane : 0].s;
   const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
   const int kl = k0 + lane < S ? k0 + lane : S - 1;
   const float2 ml0 = pml[pbase + (size_t)kl * G];
@@ -963,11 +682,9 @@ __device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, i
   // the only live ones.  The other waves' slices are live only when the
   // plan is long (a miss); they load once the plan is known.
   if (wave == 0) load_o(k0);
-  // the group's match records (uniform addresses: scalar loads) and the plan
-  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  // the head's own record (uniform address: scalar loads) and the plan
   const HeadState hs = hsg[hi];
-  int lo = hs.s;
-  for (int i = 0; i < G; ++i) lo = min(lo, hsg[i].s);
+  const int lo = wave_min_i(s_lane);
   const int n = hs.n;
   const Plan p = make_plan(lo, n, a.band, S, a.part.first);
   const int npart = p.n_pre + p.n_post;
@@ -1130,7 +847,16 @@ __global__ __launch_bounds__(MW ? 64 * kMergeMaxWaves : 64) void merge_kernel(St
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1) {
-  if (ev0) (void)hipEventRecord(ev0, st);
+  if (a.group > kMaxGroup) {
+    // wide groups (bf16 only): match launch, attention launch, merge
+    hipError_t e = launch_match_wide(a, d, st);
+    if (e != hipSuccess) return e;
+    if (ev0) (void)hipEventRecord(ev0, st);
+    e = launch_step_wide(a, d, paged, st);
+    if (e != hipSuccess) return e;
+    if (ev1) (void)hipEventRecord(ev1, st);
+  } else {
+    if (ev0) (void)hipEventRecord(ev0, st);
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
   const bool r2 = !wide && a.part.first < a.part.S;   // narrow, two rounds
@@ -1146,9 +872,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   else if (r2)                                                                                       \
     hipLaunchKernelGGL((step_kernel<T, D, false, false, true>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
-  MAC_DISPATCH(dtype, d, L_STEP);
+    MAC_DISPATCH(dtype, d, L_STEP);
 #undef L_STEP
-  if (ev1) (void)hipEventRecord(ev1, st);
+    if (ev1) (void)hipEventRecord(ev1, st);
+  }
 #define L_MERGE(T, D)                                                                              \
   if (merge_waves(a.part.S) > 1)                                                                   \
     hipLaunchKernelGGL((merge_kernel<T, D, true>), dim3(a.batch * a.hq), dim3(64 * merge_waves(a.part.S)), 0, st, a); \

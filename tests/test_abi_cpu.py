@@ -44,7 +44,9 @@ def valid_cfg(B, **kw):
 
 BAD = [
     (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(n_q_heads=30), 1),
-    (dict(n_q_heads=8 * 17), 2), (dict(head_dim=96), 2), (dict(dtype=7), 2),
+    # a group must split into equal parts of at most 32 heads (bf16) or 16 (fp32)
+    (dict(n_q_heads=8 * 33), 2), (dict(n_q_heads=8 * 17, dtype=0), 2),
+    (dict(head_dim=96), 2), (dict(dtype=7), 2),
     (dict(window=-1), 1), (dict(band=-3), 1), (dict(tau=-1.0), 1),
     (dict(tau=float("nan")), 1), (dict(rope_theta=0.0), 1),
     (dict(rope_theta=float("inf")), 1), (dict(max_slices=1), 1),
@@ -67,6 +69,13 @@ def test_bad_configs_are_rejected(B, i):
     assert st == status, B.mac_last_error()
     assert out.value is None
     assert B.mac_last_error()
+
+
+def test_wide_groups_are_accepted(B):
+    # bf16 groups of 17-32 heads run as one group, 33-64 as two equal ones
+    for hq in (8 * 17, 8 * 32, 8 * 64, 8 * 48):
+        assert B.mac_workspace_bytes(valid_cfg(B, n_q_heads=hq)) > 0
+    assert B.mac_workspace_bytes(valid_cfg(B, n_q_heads=8 * 34)) > 0
 
 
 def test_sizes_of_a_valid_config(B):

@@ -58,8 +58,9 @@ def test_noalloc_equals_the_workspace_entry_point():
             r = runs[key]
             r.out[t], r.match_n[t], r.dist[t] = (o.cpu().numpy().copy(), m.cpu().numpy().copy(),
                                                  d.cpu().numpy().copy())
+    # (rings are not compared as bytes: slots not yet written and padding
+    # hold whatever the allocator left there)
     for ref, new, w, inp in ((ref_a, new_a, wa, ia), (ref_b, new_b, wb, ib)):
-        assert torch.equal(new.ring, ref.ring)
         assert torch.equal(new.seq_lens, ref.seq_lens)
         for b in range(w.batch):       # the written keys (unwritten slots hold garbage)
             n = int(inp.contexts[b]) + T
