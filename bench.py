@@ -102,7 +102,7 @@ def step_bytes(w, n_ctx, match_n, ring_count):
 # ---------------------------------------------------------------------------
 
 class Layer:
-    def __init__(self, w, inp, n_steps, max_context):
+    def __init__(self, w, inp, n_steps, max_context, kv_layout=0):
         import torch
         from kv_cache_reuse_amd import binding as B
         self.w, self.inp = w, inp
@@ -110,10 +110,11 @@ class Layer:
             # paged cache: the stream's page table (16-token pages from a
             # shared, shuffled pool)
             cfg = B.config_from_workload(w, n_pages=int(inp.n_pages),
-                                         max_pages_per_seq=int(inp.page_table.shape[1]))
+                                         max_pages_per_seq=int(inp.page_table.shape[1]),
+                                         kv_layout=kv_layout)
             self.sess = B.MacSession(cfg, page_table=inp.page_table)
         else:
-            cfg = B.config_from_workload(w, max_context=max_context)
+            cfg = B.config_from_workload(w, max_context=max_context, kv_layout=kv_layout)
             self.sess = B.MacSession(cfg)
         dev = torch.device("cuda")
         self.K = inp.k.to(dev)
@@ -175,7 +176,7 @@ def layer_inputs(w, p_jump, per_layer, layer, inputs_cache, seed_hist=0, jumps=N
 
 
 def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefill_upto=None,
-                seed_hist=0, jumps=None):
+                seed_hist=0, jumps=None, kv_layout=0):
     """`layers` layer copies, prefilled (and, with seed_hist > 0, their rings
     seeded with the queries of the last seed_hist prefill positions).
     jumps: [layers][per_layer] bool schedules, or None for Bernoulli(p)."""
@@ -187,7 +188,7 @@ def make_layers(w, p_jump, per_layer, layers, inputs_cache, context=None, prefil
         if prefill_upto is not None:
             inp = inp.__class__(**{**inp.__dict__, "contexts": np.full(w.batch, prefill_upto)})
         mc = int(inp.contexts.max()) + per_layer if context is None else context
-        L = Layer(w, inp, per_layer, max_context=mc)
+        L = Layer(w, inp, per_layer, max_context=mc, kv_layout=kv_layout)
         L.hist = hist
         Ls.append(L)
     for L in Ls:
@@ -215,7 +216,7 @@ def layer_jump_schedules(p, steps, warmup, layers, per_layer):
 
 def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
               context=None, prefill_upto=None, inputs_cache=None, per_step=False,
-              seeded=False):
+              seeded=False, kv_layout=0):
     """warmup + steps decode steps, round-robin over `layers` layer copies.
 
     The warmup runs eagerly.  With `graph` the timed steps are captured into
@@ -232,7 +233,7 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     per_layer = (steps + warmup + layers - 1) // layers + 1
     jumps = layer_jump_schedules(p_jump, steps, warmup, layers, per_layer) if seeded else None
     Ls = make_layers(w, p_jump, per_layer, layers, inputs_cache, context, prefill_upto,
-                     seed_hist=w.window if seeded else 0, jumps=jumps)
+                     seed_hist=w.window if seeded else 0, jumps=jumps, kv_layout=kv_layout)
     torch.cuda.synchronize()
     order = [i % layers for i in range(warmup + steps)]
     for i in order[:warmup]:
@@ -748,6 +749,7 @@ def main():
     ap.add_argument("--no-batch", action="store_true")
     ap.add_argument("--no-c2", action="store_true")
     ap.add_argument("--no-c5", action="store_true")
+    ap.add_argument("--no-layout", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -816,6 +818,28 @@ def main():
                 "avg_launch_us": kern_sec * 1e6, "bytes_per_launch": kern_bytes,
                 "launches": klaunch}
     log(f"kernel: {kern_sec * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
+
+    # ---- the same step kernel on caches in the natural row layout
+    layout_ab = None
+    if not args.no_layout:
+        _, recs_r, kms_r, kl_r = run_point(w, 1.0, args.steps, args.warmup, args.layers,
+                                           kernel_timing=True, inputs_cache=cache, seeded=True,
+                                           kv_layout=1)
+        keys_r = sum(step_bytes(w, *r)[2] for r in recs_r)
+        bytes_r = keys_r * 2 * w.head_dim * w.bytes_per_elem / max(kl_r, 1)
+        us_r = 1e3 * kms_r / max(kl_r, 1)
+        msh_t, rh_t, _, _ = run_point(w, 0.0, args.steps, args.warmup, args.layers,
+                                      inputs_cache=cache, seeded=True)
+        msh_r, rh_r, _, _ = run_point(w, 0.0, args.steps, args.warmup, args.layers,
+                                      inputs_cache=cache, seeded=True, kv_layout=1)
+        layout_ab = {"workload": "8b_128k miss path (step kernel, HIP events) and all-hit step",
+                     "tiles_kernel_us": kern_sec * 1e6, "rows_kernel_us": us_r,
+                     "rows_kernel_GBps": bytes_r / us_r / 1e3,
+                     "tiles_all_hit_us_per_step": summarize(w, msh_t, rh_t, args.steps)["us_per_step"],
+                     "rows_all_hit_us_per_step": summarize(w, msh_r, rh_r, args.steps)["us_per_step"]}
+        log(f"layout A/B: step kernel tiles {kern_sec * 1e6:.1f} us, rows {us_r:.1f} us; all-hit "
+            f"step tiles {layout_ab['tiles_all_hit_us_per_step']:.2f} us, rows "
+            f"{layout_ab['rows_all_hit_us_per_step']:.2f} us")
 
     # ---- hit-rate sweep
     sweep = []
@@ -938,6 +962,7 @@ def main():
         "multilayer": multi,
         "mqa": mq,
         "configs": configs,
+        "layout_ab": layout_ab,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,

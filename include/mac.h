@@ -81,6 +81,9 @@ typedef enum {
 
 typedef enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 } mac_dtype;
 
+/* Order of the elements inside the K and V caches (see the layout note below). */
+typedef enum { MAC_KV_TILES = 0, MAC_KV_ROWS = 1 } mac_kv_layout;
+
 /* Shape and method parameters.  All fields are read at mac_init only. */
 typedef struct {
   int32_t batch;             /* sequences, >= 1                              */
@@ -98,6 +101,7 @@ typedef struct {
   float tau;                 /* >= 0; hit iff dist < tau (fp32 dist^2 test)  */
   double rope_theta;         /* > 0                                          */
   int32_t max_slices;        /* split-K slices per KV group; 0 = default     */
+  int32_t kv_layout;         /* mac_kv_layout; MAC_KV_ROWS needs bf16        */
 } mac_config;
 
 /*
@@ -121,15 +125,25 @@ typedef struct {
 typedef struct mac_ctx mac_ctx;
 
 /*
- * KV cache layout (both contiguous and paged).  Keys and values are stored
- * in tiles of 16 consecutive token positions of one (sequence, KV head).
- * Contiguous: tile (b, g, t) starts at element ((b*Hkv + g)*T + t)*16*d with
- * T = ceil(max_context/16).  Paged (page_size 16): tile t of sequence b is
- * page page_table[b*max_pages_per_seq + t], at element (page*Hkv + g)*16*d.
- * Inside a tile the 16 x d elements are permuted so that each 64-lane wave
- * load of 1 KiB lands directly in matrix-core operand order; the permutation
- * is private to the library.  Write tokens only with mac_append_kv or
- * mac_prefill_kv, read them back with mac_read_kv.
+ * KV cache layouts (abstract: the method "composes with ... paged-KV
+ * managers"; a cache is contiguous or paged, in 16-token pages).
+ *
+ * MAC_KV_ROWS, natural rows (bf16 only): element (b, g, pos, i) of a
+ *   contiguous cache is at ((b*Hkv + g)*max_context + pos)*d + i, the layout
+ *   [batch][Hkv][max_context][d]; in a paged cache (page_size 16) position
+ *   pos of sequence b is row pos % 16 of page page_table[b*max_pages_per_seq
+ *   + pos/16], element ((page*Hkv + g)*16 + pos % 16)*d + i, the layout
+ *   [n_pages][Hkv][16][d].  The caller may write tokens directly (a KV
+ *   manager's own pool) or with mac_append_kv / mac_prefill_kv.
+ * MAC_KV_TILES, library tiles (the default, both dtypes): the same 16-token
+ *   tiles (contiguous: tile (b, g, t) starts at element ((b*Hkv + g)*T + t)
+ *   *16*d with T = ceil(max_context/16); paged: as for rows), with the 16 x d
+ *   elements inside a tile permuted so that each 64-lane wave load of 1 KiB
+ *   lands directly in matrix-core operand order.  The permutation is private
+ *   to the library: write tokens only with mac_append_kv or mac_prefill_kv,
+ *   read them back with mac_read_kv.
+ * Both layouts give bitwise identical results; the tile layout spares the
+ * step kernels an LDS transpose of each value tile.
  */
 size_t mac_kv_cache_bytes(const mac_config* cfg);  /* bytes of ONE of K, V   */
 size_t mac_ring_bytes(const mac_config* cfg);      /* opaque ring            */

@@ -29,6 +29,9 @@ MAC_ERR_STATE = 5
 MAC_DTYPE_F32 = 0
 MAC_DTYPE_BF16 = 1
 
+MAC_KV_TILES = 0
+MAC_KV_ROWS = 1
+
 EXPORTED = (
     "mac_kv_cache_bytes", "mac_ring_bytes", "mac_workspace_bytes", "mac_init",
     "mac_resume", "mac_append_kv", "mac_prefill_kv", "mac_read_kv", "mac_decode_step",
@@ -50,7 +53,7 @@ class MacConfig(ctypes.Structure):
         ("head_dim", c_int32), ("dtype", c_int32), ("max_context", c_int32),
         ("page_size", c_int32), ("max_pages_per_seq", c_int32), ("n_pages", c_int32),
         ("window", c_int32), ("band", c_int32), ("tau", c_float),
-        ("rope_theta", c_double), ("max_slices", c_int32),
+        ("rope_theta", c_double), ("max_slices", c_int32), ("kv_layout", c_int32),
     ]
 
 
@@ -208,7 +211,8 @@ def mac_last_error() -> str:
 # --------------------------------------------------------------------------
 
 def config_from_workload(w, max_context: Optional[int] = None, n_pages: int = 0,
-                         max_pages_per_seq: int = 0, max_slices: int = 0) -> MacConfig:
+                         max_pages_per_seq: int = 0, max_slices: int = 0,
+                         kv_layout: int = MAC_KV_TILES) -> MacConfig:
     c = MacConfig()
     c.batch, c.n_q_heads, c.n_kv_heads = w.batch, w.n_q_heads, w.n_kv_heads
     c.head_dim = w.head_dim
@@ -220,6 +224,7 @@ def config_from_workload(w, max_context: Optional[int] = None, n_pages: int = 0,
     c.window, c.band, c.tau = w.window, w.band, float(w.tau)
     c.rope_theta = float(w.rope_theta)
     c.max_slices = max_slices
+    c.kv_layout = kv_layout
     return c
 
 

@@ -24,8 +24,8 @@ __global__ __launch_bounds__(256) void append_kernel(T* kc, T* vc, const int32_t
     const int64_t base = tile_base_w(geom, pt, b, g, t);
     if (base < 0) continue;
     const size_t src = ((size_t)b * geom.hkv + g) * D + dim;
-    kc[base + k_tile_offset<T>(r, dim)] = kn[src];
-    vc[base + v_tile_offset<T>(r, dim)] = vn[src];
+    kc[base + k_elem_offset<T>(geom, r, dim)] = kn[src];
+    vc[base + v_elem_offset<T>(geom, r, dim)] = vn[src];
   }
   __syncthreads();
   if (threadIdx.x == 0) seq_lens[b] = n0 + 1;
@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(T* kc, T* vc, const int32_
   const int64_t base = tile_base_w(geom, pt, seq, g, pos / kTile);
   if (base < 0) return;
   const size_t src = ((size_t)g * count + tok) * D + dim;
-  kc[base + k_tile_offset<T>(pos % kTile, dim)] = ks[src];
-  vc[base + v_tile_offset<T>(pos % kTile, dim)] = vs[src];
+  kc[base + k_elem_offset<T>(geom, pos % kTile, dim)] = ks[src];
+  vc[base + v_elem_offset<T>(geom, pos % kTile, dim)] = vs[src];
 }
 
 template <typename T, int D>
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void read_kernel(const T* kc, const T* vc, con
   const int pos = start + tok;
   const int64_t base = tile_base(geom, pt, seq, g, pos / kTile);
   const size_t dst = ((size_t)g * count + tok) * D + dim;
-  kd[dst] = kc[base + k_tile_offset<T>(pos % kTile, dim)];
-  vd[dst] = vc[base + v_tile_offset<T>(pos % kTile, dim)];
+  kd[dst] = kc[base + k_elem_offset<T>(geom, pos % kTile, dim)];
+  vd[dst] = vc[base + v_elem_offset<T>(geom, pos % kTile, dim)];
 }
 
 __global__ void add_len_kernel(int32_t* seq_lens, int seq, int count, int capacity) {

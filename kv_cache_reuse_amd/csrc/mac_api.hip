@@ -80,7 +80,7 @@ struct Layout {
   int slices;
   int first;            // slices per group in the first round of workgroups
   int64_t capacity;     // keys per sequence
-  int tiles_per_seq;    // contiguous cache
+  int ctx_stride;       // contiguous cache: token rows per (sequence, KV head)
 };
 
 int elem_size(int dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
@@ -130,6 +130,11 @@ mac_status check_config(const mac_config* c) {
   if (c->max_slices != 0 && (c->max_slices < 2 || c->max_slices > mac::kMaxSlices))
     return fail(MAC_ERR_INVALID_ARG, "max_slices must be 0 (default) or in [2, %d] (got %d)",
                 mac::kMaxSlices, c->max_slices);
+  if (c->kv_layout != MAC_KV_TILES && c->kv_layout != MAC_KV_ROWS)
+    return fail(MAC_ERR_INVALID_ARG, "kv_layout must be MAC_KV_TILES or MAC_KV_ROWS (got %d)",
+                c->kv_layout);
+  if (c->kv_layout == MAC_KV_ROWS && c->dtype != MAC_DTYPE_BF16)
+    return fail(MAC_ERR_UNSUPPORTED, "the row (natural) KV layout is built for bf16 caches only");
   if (c->page_size == 0) {
     if (c->max_context < 1)
       return fail(MAC_ERR_INVALID_ARG, "max_context must be >= 1 (got %d)", c->max_context);
@@ -160,7 +165,9 @@ Layout layout(const mac_config* c) {
   L.ring_bytes = off;
 
   L.capacity = c->page_size ? (int64_t)c->max_pages_per_seq * mac::kTile : (int64_t)c->max_context;
-  L.tiles_per_seq = c->page_size ? 0 : mac::ceil_div(c->max_context, mac::kTile);
+  L.ctx_stride = c->page_size ? 0
+                 : c->kv_layout == MAC_KV_ROWS ? c->max_context
+                                               : mac::ceil_div(c->max_context, mac::kTile) * mac::kTile;
   const int groups = c->batch * c->n_kv_heads * n_chunks(c);   // matched groups
   int S = c->max_slices;
   L.first = 0;
@@ -239,7 +246,8 @@ struct mac_ctx {
     mac::KvGeom g;
     g.hkv = cfg.n_kv_heads;
     g.d = cfg.head_dim;
-    g.tiles_per_seq = L.tiles_per_seq;
+    g.ctx_stride = L.ctx_stride;
+    g.natural = cfg.kv_layout == MAC_KV_ROWS ? 1 : 0;
     g.paged = cfg.page_size ? 1 : 0;
     g.max_pages = cfg.max_pages_per_seq;
     g.n_pages = cfg.n_pages;
@@ -288,7 +296,8 @@ size_t mac_kv_cache_bytes(const mac_config* cfg) {
   if (check_config(cfg)) return 0;
   const size_t tile = (size_t)mac::kTile * cfg->head_dim * elem_size(cfg->dtype);
   if (cfg->page_size) return (size_t)cfg->n_pages * cfg->n_kv_heads * tile;
-  return (size_t)cfg->batch * cfg->n_kv_heads * mac::ceil_div(cfg->max_context, mac::kTile) * tile;
+  const Layout L = layout(cfg);
+  return (size_t)cfg->batch * cfg->n_kv_heads * L.ctx_stride * cfg->head_dim * elem_size(cfg->dtype);
 }
 
 size_t mac_ring_bytes(const mac_config* cfg) {

@@ -89,14 +89,33 @@ __host__ __device__ __forceinline__ int v_tile_offset(int tok, int dim) {
   return i * (64 * E) + (lg * 16 + c) * E + th * 4 + r;
 }
 
+// Natural (row) layout, kv_layout = 1: element (token, dim) of a 16-token
+// tile at token * D + dim, the caller's [..][tokens][d] rows as they are.
+template <typename T>
+__host__ __device__ __forceinline__ int kv_row_offset(int tok, int dim, int d) {
+  return tok * d + dim;
+}
+
 struct KvGeom {
   int hkv, d;
-  int tiles_per_seq;     // contiguous: ceil(max_context / 16)
+  int ctx_stride;        // contiguous: token rows per (sequence, KV head)
+                         // (tiles: 16 * ceil(max_context / 16); rows: max_context)
   int paged;             // 1: tile t of sequence b is page_table[b*mp + t]
   int max_pages;         // paged: page-table columns
   int n_pages;           // paged: pages in the pool
   int capacity;          // keys per sequence
+  int natural;           // 1: rows in natural order (kv_layout 1), else tiles
 };
+
+// Element offsets of (token, dim) inside a tile, for either layout.
+template <typename T>
+__host__ __device__ __forceinline__ int k_elem_offset(const KvGeom& g, int tok, int dim) {
+  return g.natural ? kv_row_offset<T>(tok, dim, g.d) : k_tile_offset<T>(tok, dim);
+}
+template <typename T>
+__host__ __device__ __forceinline__ int v_elem_offset(const KvGeom& g, int tok, int dim) {
+  return g.natural ? kv_row_offset<T>(tok, dim, g.d) : v_tile_offset<T>(tok, dim);
+}
 
 // Page of tile t of sequence b; -1 if the table entry is outside the pool.
 __device__ __forceinline__ int64_t page_of(const KvGeom& g, const int32_t* pt, int b, int t) {
@@ -115,7 +134,16 @@ __device__ __forceinline__ int64_t tile_base(const KvGeom& g, const int32_t* pt,
     if (page < 0) page = 0;
     return (page * g.hkv + kvh) * tile_elems;
   }
-  return ((int64_t(b) * g.hkv + kvh) * g.tiles_per_seq + t) * tile_elems;
+  return ((int64_t(b) * g.hkv + kvh) * g.ctx_stride + int64_t(t) * kTile) * g.d;
+}
+
+// Token rows of tile t that lie inside the cache: 16, except for the last
+// tile of a contiguous natural-layout cache whose max_context is not a
+// multiple of 16 (the rows after it belong to the next KV head).
+__device__ __forceinline__ int tile_rows(const KvGeom& g, int t) {
+  if (!g.natural || g.paged) return kTile;
+  const int r = g.ctx_stride - t * kTile;
+  return r < kTile ? (r > 0 ? r : 0) : kTile;
 }
 
 // Element offset of tile t of (b, g) for writing, or -1 when position
@@ -129,7 +157,7 @@ __device__ __forceinline__ int64_t tile_base_w(const KvGeom& g, const int32_t* p
     const int64_t page = page_of(g, pt, b, t);
     return page < 0 ? -1 : (page * g.hkv + kvh) * tile_elems;
   }
-  return ((int64_t(b) * g.hkv + kvh) * g.tiles_per_seq + t) * tile_elems;
+  return ((int64_t(b) * g.hkv + kvh) * g.ctx_stride + int64_t(t) * kTile) * g.d;
 }
 
 // --------------------------------------------------------------- ring ----

@@ -24,6 +24,44 @@ constexpr int kMatchSlotsHalf = 5;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// ------------------------------------------------- natural-layout values --
+// Value tiles in the natural (row) layout arrive with lane (lg, c) holding
+// token c, bf16 elements [8 (4 j + lg), +8) of block j: the order of the key
+// operand, not of the value operand.  The wave writes the tile to LDS rows of
+// its own (ROWS = 16 rows of D + 8 elements; 16-byte aligned) and reads it
+// back in the value operand order of the library's tiles: vr[i] holds tokens
+// 4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element 4 th + r,
+// two per dword).  LDS accesses of one wave complete in order, so the reads
+// see the writes, and a later tile's writes follow this tile's reads.
+template <int D>
+struct VRows {
+  static constexpr int RS = D + 8;
+  __attribute__((aligned(16))) uint16_t v[16 * RS];
+};
+
+template <int D>
+__device__ __forceinline__ void v_rows_to_operand(VRows<D>& rows, int lane, u4 (&vr)[D / 32]) {
+  constexpr int NL = D / 32;
+  constexpr int RS = VRows<D>::RS;
+  const int lg = lane / 16, c = lane % 16;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) *reinterpret_cast<u4*>(rows.v + c * RS + 8 * (4 * j + lg)) = vr[j];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+      for (int rp = 0; rp < 2; ++rp) {
+        const int d = 16 * (2 * i + th) + c;
+        const uint32_t lo = rows.v[(4 * lg + 2 * rp) * RS + d];
+        const uint32_t hi = rows.v[(4 * lg + 2 * rp + 1) * RS + d];
+        w[2 * th + rp] = lo | (hi << 16);
+      }
+    vr[i] = u4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // Row stride of the query rows in LDS: four elements of padding, so that the
 // 16 head columns of a fragment read fall in different banks.
 __host__ __device__ constexpr int qstride(int d) { return d + 4; }

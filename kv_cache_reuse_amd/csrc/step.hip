@@ -90,7 +90,10 @@ __host__ __device__ constexpr int step_waves() {
 // group than one round fills): the slice-0 workgroup publishes its plan
 // start and second-round workgroups whose slice is empty leave early.  A
 // separate instantiation, so that one-round launches carry none of it.
-template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false>
+// NAT: caches in the natural (row) layout (bf16 only): keys load with row
+// offsets, and each value tile passes through the wave's LDS rows into the
+// value operand order.
+template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false, bool NAT = false>
 __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
   constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
   constexpr int NWB = 4;                        // waves that stream tiles
@@ -103,6 +106,8 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
   __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
+  static_assert(!NAT || BF, "the row layout is built for bf16 caches");
+  __shared__ VRows<NAT ? D : 32> vrows[NAT ? NWB : 1];
   // (padding ids of a chunked group get slice S: no plan gives it work, and
   // it writes nothing; no early return here, so that the compiler issues the
   // argument loads phase A needs together with the ones for this mapping)
@@ -123,6 +128,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   const T* vc = static_cast<const T*>(a.v_cache);
   KvGeom geom = a.geom;
   geom.paged = PAGED ? 1 : 0;
+  geom.natural = NAT ? 1 : 0;
   geom.d = D;   // a compile-time tile size in the address arithmetic
   // One tile's K and V through buffer loads: the tile's address goes into a
   // buffer descriptor in scalar registers, and each lane's byte offset
@@ -130,15 +136,21 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   // rewritten per tile (a per-tile vector address can land on a register
   // that a load in flight still targets, and the compiler then waits for
   // every load).  The descriptor covers exactly the tile.
-  const uint32_t loff = 16u * static_cast<uint32_t>(lane);
+  // (rows: lane (lg, c) reads token c's 16-byte piece 4 j + lg, block j
+  // 64 bytes further; a natural contiguous cache's last tile may hold fewer
+  // than 16 rows, and the descriptor then ends with them)
+  const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * (int)sizeof(T) + 16 * (lane / 16))
+                            : 16u * static_cast<uint32_t>(lane);
+  constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
   auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, kTile * D * (int)sizeof(T));
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, kTile * D * (int)sizeof(T));
+    const int bytes = (NAT && !PAGED ? tile_rows(geom, tt) : kTile) * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, bytes);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024u * j, 0, 0));
-      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024u * j, 0, 0));
+      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, 0));
+      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, 0));
     }
   };
 
@@ -343,11 +355,16 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
       if (patcher && tt == tnew) {
         // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
+        // (rows: V of token c, like K)
         if (col == rnew) {
 #pragma unroll
           for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(pk + E * (4 * j + lg));
+          if constexpr (NAT) {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) vr[j] = *reinterpret_cast<const u4*>(pv + E * (4 * j + lg));
+          }
         }
-        if (lg == rnew / 4) {
+        if (!NAT && lg == rnew / 4) {
 #pragma unroll
           for (int i = 0; i < NL; ++i)
 #pragma unroll
@@ -372,6 +389,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
             }
         }
       }
+      if constexpr (NAT) v_rows_to_operand<D>(vrows[wave], lane, vr);
       // ---- S = K Q^T: lane holds tokens 4 lg + r of head col
       v4f s = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF) {
@@ -538,8 +556,8 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
         T* kw = const_cast<T*>(kc);
         T* vw = const_cast<T*>(vc);
         for (int e = lane; e < D; e += 64) {
-          kw[base + k_tile_offset<T>(rnew, e)] = pk[e];
-          vw[base + v_tile_offset<T>(rnew, e)] = pv[e];
+          kw[base + k_elem_offset<T>(geom, rnew, e)] = pk[e];
+          vw[base + v_elem_offset<T>(geom, rnew, e)] = pv[e];
         }
       }
     }
@@ -860,20 +878,26 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
   const bool r2 = !wide && a.part.first < a.part.S;   // narrow, two rounds
-#define L_STEP(T, D)                                                                              \
+#define L_STEP_L(T, D, NAT)                                                                       \
   if (paged && wide)                                                                                 \
-    hipLaunchKernelGGL((step_kernel<T, D, true, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+    hipLaunchKernelGGL((step_kernel<T, D, true, true, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
   else if (paged && r2)                                                                              \
-    hipLaunchKernelGGL((step_kernel<T, D, true, false, true>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+    hipLaunchKernelGGL((step_kernel<T, D, true, false, true, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else if (paged)                                                                                    \
-    hipLaunchKernelGGL((step_kernel<T, D, true, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+    hipLaunchKernelGGL((step_kernel<T, D, true, false, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
   else if (wide)                                                                                     \
-    hipLaunchKernelGGL((step_kernel<T, D, false, true>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+    hipLaunchKernelGGL((step_kernel<T, D, false, true, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
   else if (r2)                                                                                       \
-    hipLaunchKernelGGL((step_kernel<T, D, false, false, true>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
-  else hipLaunchKernelGGL((step_kernel<T, D, false, false>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
-    MAC_DISPATCH(dtype, d, L_STEP);
+    hipLaunchKernelGGL((step_kernel<T, D, false, false, true, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+  else hipLaunchKernelGGL((step_kernel<T, D, false, false, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
+#define L_STEP(T, D) L_STEP_L(T, D, false)
+    if (a.geom.natural) {   // rows: bf16 only
+      if (d == 128) { L_STEP_L(uint16_t, 128, true); } else { L_STEP_L(uint16_t, 64, true); }
+    } else {
+      MAC_DISPATCH(dtype, d, L_STEP);
+    }
 #undef L_STEP
+#undef L_STEP_L
     if (ev1) (void)hipEventRecord(ev1, st);
   }
 #define L_MERGE(T, D)                                                                              \

@@ -111,7 +111,9 @@ struct WideShared {
 // ...).  With no match to do, the workgroup has no other waves: at one wave
 // per SIMD each wave holds both column tiles' queries and accumulators and
 // two KV tiles in flight in registers.
-template <int D, bool PAGED, int NWB>
+// NAT: caches in the natural (row) layout: keys load with row offsets and
+// each value tile passes through the wave's LDS rows into operand order.
+template <int D, bool PAGED, int NWB, bool NAT>
 __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   using T = uint16_t;
   constexpr int NTH = 64 * NWB;
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   constexpr int NC = kWideCols;
 
   __shared__ WideShared<D, NWB> sh;
+  __shared__ VRows<NAT ? D : 32> vrows[NAT ? NWB : 1];
   int grp, slice;
   step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice);
   const int b = grp / a.hkv, kvh = grp % a.hkv;
@@ -134,16 +137,20 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   const T* vc = static_cast<const T*>(a.v_cache);
   KvGeom geom = a.geom;
   geom.paged = PAGED ? 1 : 0;
+  geom.natural = NAT ? 1 : 0;
   geom.d = D;
-  const uint32_t loff = 16u * static_cast<uint32_t>(lane);
+  const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * 2 + 16 * (lane / 16))
+                            : 16u * static_cast<uint32_t>(lane);
+  constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
   auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, kTile * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, kTile * D * 2);
+    const int bytes = (NAT && !PAGED ? tile_rows(geom, tt) : kTile) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, bytes);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024u * j, 0, 0));
-      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024u * j, 0, 0));
+      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, 0));
+      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, 0));
     }
   };
 
@@ -244,11 +251,16 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
       if (patcher && tt == tnew) {
         // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
+        // (rows: V of token c, like K)
         if (col == rnew) {
 #pragma unroll
           for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(pk + E * (4 * j + lg));
+          if constexpr (NAT) {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) vr[j] = *reinterpret_cast<const u4*>(pv + E * (4 * j + lg));
+          }
         }
-        if (lg == rnew / 4) {
+        if (!NAT && lg == rnew / 4) {
 #pragma unroll
           for (int i = 0; i < NL; ++i)
 #pragma unroll
@@ -265,6 +277,7 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
             }
         }
       }
+      if constexpr (NAT) v_rows_to_operand<D>(vrows[wave], lane, vr);
       // ---- S = K Q^T for both column tiles: lane holds tokens 4 lg + r.
       // One K = 32 product per 1 KiB block: a lane's 16-byte piece (8 dims
       // of its token) is its A operand as loaded, and the same 8 dims of
@@ -394,8 +407,8 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
         T* kw = const_cast<T*>(kc);
         T* vw = const_cast<T*>(vc);
         for (int e = lane; e < D; e += 64) {
-          kw[base + k_tile_offset<T>(rnew, e)] = pk[e];
-          vw[base + v_tile_offset<T>(rnew, e)] = pv[e];
+          kw[base + k_elem_offset<T>(geom, rnew, e)] = pk[e];
+          vw[base + v_elem_offset<T>(geom, rnew, e)] = pv[e];
         }
       }
     }
@@ -459,10 +472,14 @@ hipError_t launch_match_wide(const StepArgs& a, int d, hipStream_t st) {
 hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st) {
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   constexpr int NWB = 4;
-#define L_WIDE(D)                                                                                 \
-  if (paged) hipLaunchKernelGGL((wide_step_kernel<D, true, NWB>), dim3(grid), dim3(64 * NWB), 0, st, a); \
-  else hipLaunchKernelGGL((wide_step_kernel<D, false, NWB>), dim3(grid), dim3(64 * NWB), 0, st, a)
-  if (d == 128) { L_WIDE(128); } else { L_WIDE(64); }
+#define L_WIDE(D, NAT)                                                                                 \
+  if (paged) hipLaunchKernelGGL((wide_step_kernel<D, true, NWB, NAT>), dim3(grid), dim3(64 * NWB), 0, st, a); \
+  else hipLaunchKernelGGL((wide_step_kernel<D, false, NWB, NAT>), dim3(grid), dim3(64 * NWB), 0, st, a)
+  if (a.geom.natural) {
+    if (d == 128) { L_WIDE(128, true); } else { L_WIDE(64, true); }
+  } else {
+    if (d == 128) { L_WIDE(128, false); } else { L_WIDE(64, false); }
+  }
 #undef L_WIDE
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ class GpuRun:
 
 
 def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] = None,
-                 capacity: Optional[int] = None, workspace=None):
+                 capacity: Optional[int] = None, workspace=None, kv_layout: int = 0):
     from kv_cache_reuse_amd import binding as B
     paged = bool(w.page_size) if paged is None else paged
     if paged:
@@ -40,13 +40,46 @@ def make_session(w, inp, steps: int, max_slices: int = 0, paged: Optional[bool] 
                 table = np.pad(table, ((0, 0), (0, pages - table.shape[1])))
         cfg = B.config_from_workload(w.replace(page_size=16), n_pages=int(inp.n_pages),
                                      max_pages_per_seq=int(table.shape[1]),
-                                     max_slices=max_slices)
+                                     max_slices=max_slices, kv_layout=kv_layout)
     else:
         table = None
         cfg = B.config_from_workload(w.replace(page_size=0),
                                      max_context=capacity or int(inp.contexts.max()) + steps,
-                                     max_slices=max_slices)
+                                     max_slices=max_slices, kv_layout=kv_layout)
     return B.MacSession(cfg, page_table=table, workspace=workspace)
+
+
+def write_rows(sess, w, K, V, ctx):
+    """Write tokens [0, ctx[b]) of every sequence straight into natural-row
+    caches (contiguous [batch][Hkv][max_context][d], or paged
+    [n_pages][Hkv][16][d] through the page table), then bind the context
+    again with those lengths (mac_resume keeps the ring, empty here)."""
+    from kv_cache_reuse_amd import binding as B
+    cfg = sess.cfg
+    assert cfg.kv_layout == B.MAC_KV_ROWS
+    d, hkv = cfg.head_dim, cfg.n_kv_heads
+    for b in range(w.batch):
+        n = ctx[b]
+        if cfg.page_size:
+            pages = sess.page_table[b, : -(-n // 16)].long()
+            kc = sess.k_cache.view(cfg.n_pages, hkv, 16, d)
+            vc = sess.v_cache.view(cfg.n_pages, hkv, 16, d)
+            kp = torch.zeros((pages.numel() * 16, hkv, d), dtype=K.dtype, device=K.device)
+            vp = torch.zeros_like(kp)
+            kp[:n] = K[b, :, :n].transpose(0, 1)
+            vp[:n] = V[b, :, :n].transpose(0, 1)
+            kc[pages] = kp.view(-1, 16, hkv, d).transpose(1, 2)
+            vc[pages] = vp.view(-1, 16, hkv, d).transpose(1, 2)
+        else:
+            kc = sess.k_cache.view(cfg.batch, hkv, cfg.max_context, d)
+            vc = sess.v_cache.view(cfg.batch, hkv, cfg.max_context, d)
+            kc[b, :, :n] = K[b, :, :n]
+            vc[b, :, :n] = V[b, :, :n]
+    sess.seq_lens.copy_(torch.tensor(ctx, dtype=torch.int32, device=sess.seq_lens.device))
+    torch.cuda.synchronize()
+    B.mac_destroy(sess.ctx)
+    sess.ctx = B.mac_resume(cfg, sess.ring.data_ptr(), sess.workspace.data_ptr(),
+                            sess.seq_lens.data_ptr(), ctx, sess._s())
 
 
 def step_inputs(w, inp, dev):
@@ -126,22 +159,30 @@ def run_layers(w, inps, steps: Optional[int] = None, capacity: Optional[int] = N
 
 def run_gpu(w, inp, steps: Optional[int] = None, record=None, max_slices: int = 0,
             paged: Optional[bool] = None, q_override=None, poison: bool = False,
-            fused: bool = False, seed_q=None, capacity: Optional[int] = None) -> GpuRun:
+            fused: bool = False, seed_q=None, capacity: Optional[int] = None,
+            kv_layout: int = 0, direct_prefill: bool = False) -> GpuRun:
     """Prefill every sequence, optionally seed the rings with the queries
     `seed_q` [n, batch, Hq, d] of the last n prefill positions, then
     `steps` x (append, decode).  `record` selects the steps whose outputs are
     copied back (default: all)."""
     T = inp.q.shape[0] if steps is None else steps
     dev = torch.device("cuda")
-    sess = make_session(w, inp, T, max_slices=max_slices, paged=paged, capacity=capacity)
+    sess = make_session(w, inp, T, max_slices=max_slices, paged=paged, capacity=capacity,
+                        kv_layout=kv_layout)
     if poison:                       # stale NaN in every slot not yet written
         sess.k_cache.fill_(float("nan"))
         sess.v_cache.fill_(float("nan"))
     K = inp.k.to(dev)
     V = inp.v.to(dev)
     ctx = [int(c) for c in inp.contexts]
-    for b in range(w.batch):
-        sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
+    if direct_prefill:
+        # natural rows: the caller writes the prefill into the caches itself
+        # (as a KV manager that owns the pool would) and starts the context
+        # with those lengths
+        write_rows(sess, w, K, V, ctx)
+    else:
+        for b in range(w.batch):
+            sess.prefill(b, K[b, :, :ctx[b]], V[b, :, :ctx[b]])
     if seed_q is not None:
         sess.seed(seed_q.to(dev).contiguous())
     q_all = (inp.q if q_override is None else q_override).to(dev)
