@@ -58,7 +58,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_step_kernel_8b_128k.js
 # sources the step kernel is compiled from: the stored counter figures are
 # only valid for the kernel they were taken on
 KERNEL_SRCS = [os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", f)
-               for f in ("step.hip", "mac_dev.h")]
+               for f in ("step.hip", "match.h", "mac_dev.h")]
 ROOFLINE_KERNEL = "mac::step_kernel<bf16,128,contiguous>"
 COPY_CAL_BYTES = 512 * 1024 * 1024
 
@@ -511,7 +511,7 @@ CONFIG_POINTS = {
 }
 
 
-def config_point(key, steps, warmup, cache, miss=True, classes=False):
+def config_point(key, steps, warmup, cache, miss=True, classes=False, streams=True):
     """One workload of the configs: its miss path (every token jumps), graph-
     replayed, with the step kernel timed by HIP events in an eager run (that
     kernel's roofline at this shape); its own query stream (its jump
@@ -537,7 +537,7 @@ def config_point(key, steps, warmup, cache, miss=True, classes=False):
         log(f"  {key} miss: {st['us_per_step']:.1f} us/step ({st['eff_GBps']:.0f} GB/s), step "
             f"kernel {kus:.1f} us = {kbytes / kus / 1e3:.0f} GB/s "
             f"({100 * kbytes / kus / 1e3 / HBM_PEAK_GBPS:.1f} % of 8 TB/s)")
-    for label, p in (("stream", w.p_jump), ("all_hit", 0.0)):
+    for label, p in ((("stream", w.p_jump), ("all_hit", 0.0)) if streams else ()):
         msp, rp, _, _ = run_point(w, p, steps, warmup, layers, inputs_cache=cache, seeded=True)
         sp = summarize(w, msp, rp, steps)
         res[label] = {"p_jump": p, "us_per_step": sp["us_per_step"],
@@ -758,6 +758,8 @@ def main():
                     help="first copy 512 MiB device-to-device (counter calibration)")
     ap.add_argument("--config-only", type=str, default="",
                     help="run only this config point (for profiling its kernels) and print it")
+    ap.add_argument("--miss-only", action="store_true",
+                    help="with --config-only: the miss path only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step "
@@ -788,7 +790,7 @@ def main():
             sys.exit(2)
         log(f"config point {key} only")
         res = config_point(key, args.steps, args.warmup, cache,
-                           miss=key != "70b_128k_rho_per_kv")
+                           miss=key != "70b_128k_rho_per_kv", streams=not args.miss_only)
         print(json.dumps({"config_only": key, **res}), flush=True)
         return
 

@@ -319,8 +319,10 @@ mac_status mac_seed_ring(mac_ctx* ctx, const void* q_hist, int n_hist,
 
 /*
  * Kernel timing for measurement.  While enabled, each mac_decode_step
- * records a pair of HIP events around its split-K attention launch on the
- * step's stream (at most 65536 pairs are kept).  mac_profile_read waits for
+ * times its split-K attention kernel with a pair of HIP events on the step's
+ * stream, bound to the kernel's dispatch (recorded as the kernel starts and
+ * ends, so host enqueue time is not included; at most 65536 pairs are
+ * kept).  mac_profile_read waits for
  * the recorded events, returns the summed milliseconds and the number of
  * launches timed, and clears the record.
  */

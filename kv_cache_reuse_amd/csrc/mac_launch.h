@@ -1,14 +1,26 @@
 // Host-side launchers of the libmac kernels (internal C++ interface).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "mac_dev.h"
 
 namespace mac {
 
+// Launch of a step's attention kernel.  With timing events, they are bound
+// to the kernel's own dispatch (recorded when it starts and when it ends), so
+// the measured time holds the kernel alone, also when the host enqueues
+// slower than the GPU runs.
+template <typename K>
+inline void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t ev0,
+                             hipEvent_t ev1, const StepArgs& a) {
+  if (ev0) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev0, ev1, 0, a);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+}
+
 // match -> split-K attention -> merge, on `st`.  If ev0/ev1 are non-null they
-// are recorded right before and after the split-K attention launch.
+// time the split-K attention kernel (launch_attention).
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1);
 
@@ -16,7 +28,8 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
 // every query head (records, rotated queries, reused states) and the split-K
 // attention that reads them (wide.hip).
 hipError_t launch_match_wide(const StepArgs& a, int d, hipStream_t st);
-hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st);
+hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1);
 
 hipError_t launch_append(void* kc, void* vc, const int32_t* pt, const void* kn, const void* vn,
                          int32_t* seq_lens, const KvGeom& geom, int batch, int dtype,

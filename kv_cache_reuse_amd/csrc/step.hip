@@ -869,27 +869,24 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
     // wide groups (bf16 only): match launch, attention launch, merge
     hipError_t e = launch_match_wide(a, d, st);
     if (e != hipSuccess) return e;
-    if (ev0) (void)hipEventRecord(ev0, st);
-    e = launch_step_wide(a, d, paged, st);
+    e = launch_step_wide(a, d, paged, st, ev0, ev1);
     if (e != hipSuccess) return e;
-    if (ev1) (void)hipEventRecord(ev1, st);
   } else {
-    if (ev0) (void)hipEventRecord(ev0, st);
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
   const bool r2 = !wide && a.part.first < a.part.S;   // narrow, two rounds
 #define L_STEP_L(T, D, NAT)                                                                       \
   if (paged && wide)                                                                                 \
-    hipLaunchKernelGGL((step_kernel<T, D, true, true, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+    launch_attention(step_kernel<T, D, true, true, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, true>()), st, ev0, ev1, a); \
   else if (paged && r2)                                                                              \
-    hipLaunchKernelGGL((step_kernel<T, D, true, false, true, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+    launch_attention(step_kernel<T, D, true, false, true, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a); \
   else if (paged)                                                                                    \
-    hipLaunchKernelGGL((step_kernel<T, D, true, false, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
+    launch_attention(step_kernel<T, D, true, false, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a); \
   else if (wide)                                                                                     \
-    hipLaunchKernelGGL((step_kernel<T, D, false, true, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, true>()), 0, st, a); \
+    launch_attention(step_kernel<T, D, false, true, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, true>()), st, ev0, ev1, a); \
   else if (r2)                                                                                       \
-    hipLaunchKernelGGL((step_kernel<T, D, false, false, true, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a); \
-  else hipLaunchKernelGGL((step_kernel<T, D, false, false, false, NAT>), dim3(grid), dim3(64 * step_waves<T, D, false>()), 0, st, a)
+    launch_attention(step_kernel<T, D, false, false, true, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a); \
+  else launch_attention(step_kernel<T, D, false, false, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a)
 #define L_STEP(T, D) L_STEP_L(T, D, false)
     if (a.geom.natural) {   // rows: bf16 only
       if (d == 128) { L_STEP_L(uint16_t, 128, true); } else { L_STEP_L(uint16_t, 64, true); }
@@ -898,7 +895,6 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
     }
 #undef L_STEP
 #undef L_STEP_L
-    if (ev1) (void)hipEventRecord(ev1, st);
   }
 #define L_MERGE(T, D)                                                                              \
   if (merge_waves(a.part.S) > 1)                                                                   \

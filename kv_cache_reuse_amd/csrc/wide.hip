@@ -469,12 +469,13 @@ hipError_t launch_match_wide(const StepArgs& a, int d, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st) {
+hipError_t launch_step_wide(const StepArgs& a, int d, int paged, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   constexpr int NWB = 4;
 #define L_WIDE(D, NAT)                                                                                 \
-  if (paged) hipLaunchKernelGGL((wide_step_kernel<D, true, NWB, NAT>), dim3(grid), dim3(64 * NWB), 0, st, a); \
-  else hipLaunchKernelGGL((wide_step_kernel<D, false, NWB, NAT>), dim3(grid), dim3(64 * NWB), 0, st, a)
+  if (paged) launch_attention(wide_step_kernel<D, true, NWB, NAT>, dim3(grid), dim3(64 * NWB), st, ev0, ev1, a); \
+  else launch_attention(wide_step_kernel<D, false, NWB, NAT>, dim3(grid), dim3(64 * NWB), st, ev0, ev1, a)
   if (a.geom.natural) {
     if (d == 128) { L_WIDE(128, true); } else { L_WIDE(64, true); }
   } else {
