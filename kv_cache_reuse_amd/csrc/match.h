@@ -212,21 +212,35 @@ __device__ __forceinline__ void match_load(const StepArgs& a, int bh, int lane, 
   load_slots<T, D, KMS>(a, bh, lane, 0, st, off, mi);
 }
 
-// Rotate-half pairs (i, i + D/2) of head hi's query: float64 angle and
-// rotation, result scaled by log2(e)/sqrt(D) so that the attention can use
-// exp2; pairs i0 <= i < i1 are stored in LDS as bf16 hi/lo halves (or fp32).
-// Every lane that loaded a pair computes it, so the loads are consumed.
+// The rotation of pair i at position pos: the angle pos * theta^(-2i/d) in
+// float64 (pos reaches 1e5 and more, where a float32 angle errs by about
+// 1e-2 rad), reduced to [-pi, pi] in float64 (Cody-Waite, 2 pi split into a
+// 53-bit head and its tail), then sine and cosine in float32.
+__device__ __forceinline__ void rope_sincos(int pos, double inv, float* sn, float* cs) {
+  constexpr double kInv2Pi = 0.15915494309189533577;
+  constexpr double k2PiHi = 6.28318530717958623200;    // nearest double to 2 pi
+  constexpr double k2PiLo = 2.44929359829470635445e-16; // 2 pi - k2PiHi
+  const double ang = static_cast<double>(pos) * inv;
+  const double k = rint(ang * kInv2Pi);
+  const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, ang));
+  sincosf(static_cast<float>(r), sn, cs);
+}
+
+// Rotate-half pairs (i, i + D/2) of head hi's query (angle as rope_sincos),
+// result scaled by log2(e)/sqrt(D) so that the attention can use exp2; pairs
+// i0 <= i < i1 are stored in LDS as bf16 hi/lo halves (or fp32).  Every lane
+// that loaded a pair computes it, so the loads are consumed.
 template <typename T, int D, int KMS, class SH>
 __device__ __forceinline__ void rope_q(SH& sh, int hi, int lane, int n, const MatchIn<T, D, KMS>& mi,
                                        int i0 = 0, int i1 = D / 2) {
   if (lane < D / 2) {
     const int i = lane;
-    double sn, cs;
-    sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
-    const double x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
-    const double sc = kLog2e / sqrt(static_cast<double>(D));
-    const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
-    const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
+    float sn, cs;
+    rope_sincos(n - 1, mi.inv, &sn, &cs);
+    const float x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
+    const float sc = static_cast<float>(kLog2e / sqrt(static_cast<double>(D)));
+    const float r1 = fmaf(x1, cs, -x2 * sn) * sc;
+    const float r2 = fmaf(x2, cs, x1 * sn) * sc;
     if (i < i0 || i >= i1) return;
     if constexpr (sizeof(T) == 2) {
       uint16_t* qh = reinterpret_cast<uint16_t*>(sh.q) + hi * qstride(D);

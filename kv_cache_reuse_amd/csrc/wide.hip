@@ -60,12 +60,12 @@ __global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
   // rotate-half pairs (i, i + D/2) at position n - 1, float64 angle and
   // rotation, scaled so that the attention can use exp2; hi and lo halves
   if (lane < D / 2) {
-    double sn, cs;
-    sincos(static_cast<double>(n - 1) * mi.inv, &sn, &cs);
-    const double x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
-    const double sc = kLog2e / sqrt(static_cast<double>(D));
-    const float r1 = static_cast<float>((x1 * cs - x2 * sn) * sc);
-    const float r2 = static_cast<float>((x2 * cs + x1 * sn) * sc);
+    float sn, cs;
+    rope_sincos(n - 1, mi.inv, &sn, &cs);
+    const float x1 = from_bits<T>(mi.q1), x2 = from_bits<T>(mi.q2);
+    const float sc = static_cast<float>(kLog2e / sqrt(static_cast<double>(D)));
+    const float r1 = fmaf(x1, cs, -x2 * sn) * sc;
+    const float r2 = fmaf(x2, cs, x1 * sn) * sc;
     uint16_t* qh = wide_qrot(a) + static_cast<size_t>(bh) * 2 * D;
     uint16_t* ql = qh + D;
     const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
