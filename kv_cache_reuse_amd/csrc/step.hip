@@ -874,7 +874,11 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
   } else {
   const int grid = step_grid(a.batch * a.hkv, a.nchunk, a.part.S);
   const bool wide = a.group > 4;
-  const bool r2 = !wide && a.part.first < a.part.S;   // narrow, two rounds
+  // narrow, more than one round of workgroups: later rounds leave early on
+  // hits.  (Wide groups measured slower with it: on the 70B shape, whose
+  // groups rarely all hit, every later-round workgroup waits for the check
+  // before its first tile load.)
+  const bool r2 = !wide && a.part.first < a.part.S;
 #define L_STEP_L(T, D, NAT)                                                                       \
   if (paged && wide)                                                                                 \
     launch_attention(step_kernel<T, D, true, true, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, true>()), st, ev0, ev1, a); \

@@ -115,6 +115,22 @@ def test_two_rounds_every_step(fused, page_size, capacity):
     assert_report(rep, f"rounds:{fused}:{page_size}:{capacity}")
 
 
+@pytest.mark.parametrize("fused,page_size", [(False, 0), (True, 0), (True, 16)])
+def test_wide_groups_in_two_rounds(fused, page_size):
+    # groups of 8 query heads (the 70B shape) with a capacity that gives the
+    # launch three rounds of workgroups (the later rounds run every match
+    # and take their slices of the plan)
+    w = workload("70b_128k", batch=2, page_size=page_size, context=2000, steps=24)
+    if page_size:
+        w = w.replace(ctx_range=(1500, 2500))
+    say(f"[wide rounds fused={fused} page_size={page_size}] {w}")
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp, capacity=140000, fused=fused)   # 16 groups: 3 rounds of 16 slices
+    assert gpu.session.cfg.max_slices == 0
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, f"wide_rounds:{fused}:{page_size}")
+
+
 @pytest.mark.parametrize("batch", [16, 17])
 def test_later_rounds_at_the_order_limits(batch):
     # 16 sequences fill every entry of the later rounds' sequence order; 17
