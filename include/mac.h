@@ -88,8 +88,9 @@ typedef enum { MAC_KV_TILES = 0, MAC_KV_ROWS = 1 } mac_kv_layout;
 typedef struct {
   int32_t batch;             /* sequences, >= 1                              */
   int32_t n_q_heads;         /* Hq, a multiple of n_kv_heads                 */
-  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv <= 16, or G splitting into */
-                             /* ceil(G/16) equal groups (MQA: 32, 64, ...)   */
+  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv <= C, or G splitting into  */
+                             /* ceil(G/C) equal groups of at most C heads:   */
+                             /* C = 32 for bf16 (MQA: 32, 64, ...), 16 fp32  */
   int32_t head_dim;          /* d: 64 or 128                                 */
   int32_t dtype;             /* mac_dtype of q, keys, values and ring q      */
   int32_t max_context;       /* contiguous cache: keys per sequence          */
@@ -107,19 +108,22 @@ typedef struct {
 /*
  * Default slice count (max_slices = 0): base = ceil(256 / groups) slices per
  * KV group, one workgroup per compute unit, where groups = batch * Hkv *
- * ceil(G/16).  When a full-length sequence's base slices would hold more than
- * about 6K keys, the launch takes further rounds of as many workgroups, one
- * per 4096 keys a first-round slice would hold, at most 4 rounds.  The
- * hardware deals the later rounds to compute units as they come free; on a
- * step where a group's heads all hit, its later-round workgroups leave as
- * soon as they read the group's plan, and for 2 to 16 sequences the later
- * rounds visit the sequences longest first (by the host's length mirror at
- * the call).  The early exit and the ordering apply to groups of at most 4
- * query heads; wider groups run every later-round workgroup's match.  The
- * count is capped by ceil(capacity / 64) + 1, by 1024 and
- * by G * slices <= 2048, and is at least 2.  An explicit max_slices (also
- * capped by G * slices <= 2048) runs all its slices in one round.  The slice
- * count fixes mac_workspace_bytes.
+ * ceil(G/C) (C as for n_kv_heads).  When a full-length sequence's base
+ * slices would hold more than about 6K keys, the launch takes further rounds
+ * of as many workgroups, one per 4096 keys a first-round slice would hold,
+ * at most 4 rounds.  The hardware deals the later rounds to compute units as
+ * they come free.  On a step where a group's heads all hit, its later-round
+ * workgroups leave as soon as they read the group's plan, and for 2 to 16
+ * sequences the later rounds visit the sequences longest first (by the
+ * host's length mirror at the call); both apply to groups of at most 4 query
+ * heads.  Wider groups run every later-round workgroup's match, except bf16
+ * groups of more than 16 heads: matched in a launch of their own, their
+ * later-round workgroups leave an empty slice once they have read the
+ * group's match records.  The count is capped by ceil(capacity / 64) + 1, by
+ * 1024 and by G' * slices <= 2048 (8192 for bf16 groups of more than 16
+ * heads), G' the heads per group, and is at least 2.  An explicit
+ * max_slices (capped by the G' * slices bound only) runs all its slices in
+ * one round.  The slice count fixes mac_workspace_bytes.
  */
 
 typedef struct mac_ctx mac_ctx;

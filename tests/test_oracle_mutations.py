@@ -68,12 +68,34 @@ def match_oldest_on_ties(q, ring, tau, p_new):
     return M.Match(best, best >= 0 and best_d < tau, best_d, dists)
 
 
+def match_non_strict(q, ring, tau, p_new):
+    # hit when the distance equals tau
+    m = ORIG_MATCH(q, ring, tau, p_new)
+    return M.Match(m.j, m.j >= 0 and m.dist <= tau, m.dist, m.dists)
+
+
+def match_any_prefix(q, ring, tau, p_new):
+    # candidates whose cached prefix passes the current one are not skipped
+    dists = np.full(len(ring), np.nan)
+    best, best_d = -1, np.inf
+    for j in range(len(ring) - 1, -1, -1):
+        dj = float(np.sqrt(np.sum((q - ring[j].q) ** 2)))
+        dists[j] = dj
+        if dj < best_d:
+            best, best_d = j, dj
+    return M.Match(best, best >= 0 and best_d < tau, best_d, dists)
+
+
+ORIG_MATCH = M.match
+
 MUTANTS = [
     ("rope", rope_sign_flip, [P.test_rope_matches_complex_rotation]),
     ("rope", rope_adjacent_pairs, [P.test_rope_matches_complex_rotation]),
     ("merge", merge_without_rescale, [lambda: P.test_merge_of_any_partition_equals_single_pass(1.0)]),
     ("attend", attend_wrong_scale, [P.test_attend_equals_scipy_softmax_attention]),
     ("match", match_oldest_on_ties, [P.test_match_golden_ties_and_strictness]),
+    ("match", match_non_strict, [P.test_match_golden_ties_and_strictness]),
+    ("match", match_any_prefix, [P.test_match_skips_entries_whose_prefix_passes_the_current_one]),
     # a hit that skips the band: fresh attention from the matched entry's
     # context end instead of its prefix end
     ("fresh_start", lambda e: e.n,
