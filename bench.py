@@ -469,6 +469,11 @@ def multilayer(layers=32, tokens=32):
     return out
 
 
+# One MQA layer's cache is 67 MB: eight copies (537 MB) keep the steps from
+# finding their keys in the 256 MB last-level cache.
+MQA_LAYERS = 8
+
+
 def mqa(steps, warmup, cache=None):
     """MQA at the headline context: 32 query heads over one KV head (one
     32-head group: a match launch, then one pass over the tiles for all its
@@ -478,15 +483,17 @@ def mqa(steps, warmup, cache=None):
     w = workload("8b_128k", n_kv_heads=1)
     # step time from the graph replay; the step kernel's duration from an
     # eager run with HIP events around it
-    ms, recs, _, _ = run_point(w, 1.0, steps, warmup, 2, inputs_cache=cache)
+    ms, recs, _, _ = run_point(w, 1.0, steps, warmup, MQA_LAYERS, inputs_cache=cache)
     st = summarize(w, ms, recs, steps)
-    _, recs_k, kms, kl = run_point(w, 1.0, steps, warmup, 2, kernel_timing=True,
+    _, recs_k, kms, kl = run_point(w, 1.0, steps, warmup, MQA_LAYERS, kernel_timing=True,
                                    inputs_cache=cache)
     keys = sum(step_bytes(w, *r)[2] for r in recs_k)
     kbytes = keys * 2 * w.head_dim * w.bytes_per_elem / max(kl, 1)
-    msh, rh, _, _ = run_point(w, 0.0, steps, warmup, 2, inputs_cache=cache, seeded=True)
+    msh, rh, _, _ = run_point(w, 0.0, steps, warmup, MQA_LAYERS, inputs_cache=cache, seeded=True)
     sh = summarize(w, msh, rh, steps)
-    res = {"workload": "8b_128k with 1 KV head: 32 query heads in one group (a match launch, then one pass over the tiles for all 32 heads)",
+    res = {"workload": "8b_128k with 1 KV head: 32 query heads in one group (a match launch, then "
+                       f"one pass over the tiles for all 32 heads); {MQA_LAYERS} layer copies "
+                       "visited in turn",
            "miss_us_per_step": st["us_per_step"], "miss_kernel_us": 1e3 * kms / max(kl, 1),
            "miss_kernel_GBps": kbytes / (kms / 1e3 / max(kl, 1)) / 1e9,
            "hit_us_per_step": sh["us_per_step"], "hit_rate": sh["hit_rate"]}
@@ -559,36 +566,39 @@ def config_point(key, steps, warmup, cache, miss=True, classes=False, streams=Tr
 def read_ceiling():
     """HBM read rate of a plain streaming-read kernel (libmac_bw.so) over a
     2 GiB buffer (8x the last-level cache): the best of a few grid sizes,
-    each timed with HIP events."""
+    with default and with non-temporal loads, each timed with HIP events."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_reuse_amd", "libmac_bw.so"))
     lib.mac_bw_read.restype = ctypes.c_int
     lib.mac_bw_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+                                ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
     sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    best = (0.0, 0)
-    for blocks in (512, 1024, 2048, 4096, 8192, 16384):
-        for rep_ in range(4):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            st = lib.mac_bw_read(buf.data_ptr(), nbytes, sink.data_ptr(), 0x9e3779b9, blocks,
-                                 stream.cuda_stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if st != 0:
-                raise RuntimeError(f"mac_bw_read failed with HIP error {st}")
-            if rep_ > 0:
-                gbps = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
-                best = max(best, (gbps, blocks))
+    best = {0: (0.0, 0), 1: (0.0, 0)}
+    for nt in (0, 1):
+        for blocks in (512, 1024, 2048, 4096, 8192, 16384):
+            for rep_ in range(4):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st = lib.mac_bw_read(buf.data_ptr(), nbytes, sink.data_ptr(), 0x9e3779b9, blocks,
+                                     nt, stream.cuda_stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if st != 0:
+                    raise RuntimeError(f"mac_bw_read failed with HIP error {st}")
+                if rep_ > 0:
+                    gbps = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+                    best[nt] = max(best[nt], (gbps, blocks))
     del buf
     torch.cuda.empty_cache()
-    return {"GBps": best[0], "blocks": best[1], "bytes": nbytes,
-            "pct_hbm_peak": 100.0 * best[0] / HBM_PEAK_GBPS}
+    top = max(best.values())
+    return {"GBps": top[0], "blocks": top[1], "bytes": nbytes,
+            "pct_hbm_peak": 100.0 * top[0] / HBM_PEAK_GBPS,
+            "default_loads_GBps": best[0][0], "nontemporal_loads_GBps": best[1][0]}
 
 
 def summarize(w, ms, recs, steps):
@@ -915,14 +925,15 @@ def main():
     mq = None
     if not args.no_mqa:
         log("MQA: 32 query heads over 1 KV head at 131072 keys")
-        mq = mqa(min(args.steps, 128), args.warmup)
+        mq = mqa(min(args.steps, 128), args.warmup, {})
 
     # ---- streaming-read ceiling of this device, same run
     ceil = None
     if not args.no_ceiling:
         ceil = read_ceiling()
         roofline["pct_of_read_ceiling"] = 100.0 * achieved / ceil["GBps"]
-        log(f"read ceiling: {ceil['GBps']:.0f} GB/s ({ceil['pct_hbm_peak']:.1f} % of peak); "
+        log(f"read ceiling: {ceil['GBps']:.0f} GB/s ({ceil['pct_hbm_peak']:.1f} % of peak; default "
+            f"loads {ceil['default_loads_GBps']:.0f}, non-temporal {ceil['nontemporal_loads_GBps']:.0f}); "
             f"step kernel at {roofline['pct_of_read_ceiling']:.1f} % of it")
 
     cpu = None

@@ -12,7 +12,15 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // Each workgroup streams its own contiguous chunk of the buffer, every thread
 // keeping 8 16-byte loads in flight, and folds them with xor; the fold is
 // stored only when it equals a value the caller passes (practically never),
-// which keeps the loads alive.
+// which keeps the loads alive.  NT: non-temporal loads (lines not kept for
+// reuse), the policy the decode step streams its long key ranges with.
+template <bool NT>
+__device__ __forceinline__ u4 load16(const u4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const u4* __restrict__ buf, size_t n16,
                                                    uint32_t* sink, uint32_t magic) {
   const size_t per = n16 / gridDim.x;
@@ -23,11 +31,11 @@ __global__ __launch_bounds__(256) void read_kernel(const u4* __restrict__ buf, s
   for (; i + 7 * 256 < end; i += 8 * 256) {
     u4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
+    for (int u = 0; u < 8; ++u) v[u] = load16<NT>(p + i + u * 256);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
-  for (; i < end; i += 256) acc ^= p[i];
+  for (; i < end; i += 256) acc ^= load16<NT>(p + i);
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == magic) sink[blockIdx.x] = x;
 }
@@ -35,13 +43,16 @@ __global__ __launch_bounds__(256) void read_kernel(const u4* __restrict__ buf, s
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from the device buffer `buf` with `blocks`
-// workgroups of 256 threads on `stream`.  `sink` is a device array of
-// `blocks` words, written only where a chunk's xor equals `magic`.  Returns
-// the HIP error code.
+// workgroups of 256 threads on `stream`, with non-temporal loads if
+// `nontemporal` is nonzero.  `sink` is a device array of `blocks` words,
+// written only where a chunk's xor equals `magic`.  Returns the HIP error
+// code.
 extern "C" int mac_bw_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t magic,
-                           int blocks, void* stream) {
+                           int blocks, int nontemporal, void* stream) {
   if (!buf || !sink || bytes % 16 != 0 || blocks <= 0) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u4*>(buf), bytes / 16, sink, magic);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u4* p = static_cast<const u4*>(buf);
+  if (nontemporal) hipLaunchKernelGGL(read_kernel<true>, dim3(blocks), dim3(256), 0, st, p, bytes / 16, sink, magic);
+  else hipLaunchKernelGGL(read_kernel<false>, dim3(blocks), dim3(256), 0, st, p, bytes / 16, sink, magic);
   return (int)hipGetLastError();
 }

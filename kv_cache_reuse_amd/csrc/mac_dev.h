@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mac {
 
 constexpr int kTile = 16;        // tokens per KV tile (= page size when paged)
@@ -20,6 +22,12 @@ constexpr int kMergeCap = 2048;  // most (query head, slice) pairs one merge hol
 // kWideGroup heads, two matrix-core column tiles per key fragment.
 constexpr int kWideGroup = 32;
 constexpr int kMergeCapWide = 8192;
+
+// Cache policy of the KV tile loads, the cache-policy operand of the buffer
+// load instruction: kKeep, the default; kStream, non-temporal (the "nt"
+// bit: lines are not kept for reuse), for keys a step streams once.
+constexpr std::integral_constant<int, 0> kKeep{};
+constexpr std::integral_constant<int, 2> kStream{};
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));

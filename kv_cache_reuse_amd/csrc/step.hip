@@ -142,17 +142,20 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * (int)sizeof(T) + 16 * (lane / 16))
                             : 16u * static_cast<uint32_t>(lane);
   constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
-  auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
+  // cpol: the loads' cache policy (kCachePolicyKeep or kCachePolicyStream),
+  // a compile-time constant of the instruction
+  auto load_tile_p = [&](auto cpol, int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
     const int bytes = (NAT && !PAGED ? tile_rows(geom, tt) : kTile) * D * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, bytes);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, 0));
-      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, 0));
+      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, decltype(cpol)::value));
+      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, decltype(cpol)::value));
     }
   };
+  auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) { load_tile_p(kKeep, tt, kk, vv); };
 
   // ---------------------------------------------------------------- A ----
   // the match loads of this wave's first head go out before the length
@@ -512,25 +515,35 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     const int tlast = t1 - 1;
     const int tw = t0 + wave;
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
-    if (nt > 0) {
+    // The slices before p_new stream their keys once per step (on a miss,
+    // nearly the whole cache), so their loads take the streaming policy and
+    // leave the caches to what is read again: the slices after p_new hold
+    // the band and the tail, which the next steps read again whether they
+    // hit or miss.  (Each policy has its own copy of the loop, chosen
+    // before it, so no load sits under a branch inside it.)
+    auto stream = [&](auto cpol) {
       u4 kB[NL], vB[NL];
-      if (tw != tspec) load_tile(tw, kA, vA);
+      if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
       int i = 0;
       for (; i + 2 < nt; i += 2) {
         const int t = tw + NWB * i;
-        load_tile(t + NWB, kB, vB);
+        load_tile_p(cpol, t + NWB, kB, vB);
         process(t, kA, vA);
-        load_tile(min(t + 2 * NWB, tlast), kA, vA);
+        load_tile_p(cpol, min(t + 2 * NWB, tlast), kA, vA);
         process(t + NWB, kB, vB);
       }
       if (i + 1 < nt) {
         const int t = tw + NWB * i;
-        load_tile(t + NWB, kB, vB);
+        load_tile_p(cpol, t + NWB, kB, vB);
         process(t, kA, vA);
         process(t + NWB, kB, vB);
       } else {
         process(tw + NWB * i, kA, vA);
       }
+    };
+    if (nt > 0) {
+      if (slice_is_pre(p, slice)) stream(kStream);
+      else stream(kKeep);
     }
     // slice 0 publishes the plan start for the second round of workgroups.
     // The store comes after the tile loop in program order (a global store

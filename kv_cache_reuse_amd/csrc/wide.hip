@@ -142,17 +142,18 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * 2 + 16 * (lane / 16))
                             : 16u * static_cast<uint32_t>(lane);
   constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
-  auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
+  auto load_tile_p = [&](auto cpol, int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
     const int bytes = (NAT && !PAGED ? tile_rows(geom, tt) : kTile) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, bytes);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, 0));
-      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, 0));
+      kk[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + kBlockStep * j, 0, decltype(cpol)::value));
+      vv[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + kBlockStep * j, 0, decltype(cpol)::value));
     }
   };
+  auto load_tile = [&](int tt, u4 (&kk)[NL], u4 (&vv)[NL]) { load_tile_p(kKeep, tt, kk, vv); };
 
   // ---------------------------------------------------------------- A ----
   // The group's match records and rotated queries do not depend on the
@@ -373,25 +374,32 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     const int tlast = t1 - 1;
     const int tw = t0 + wave;
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
-    if (nt > 0) {
+    // slices before p_new stream with the non-temporal policy, the band and
+    // the tail (read again by the next steps) with the default one; one
+    // copy of the loop per policy
+    auto stream = [&](auto cpol) {
       u4 kB[NL], vB[NL];
-      if (tw != tspec) load_tile(tw, kA, vA);
+      if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
       int i = 0;
       for (; i + 2 < nt; i += 2) {
         const int t = tw + NWB * i;
-        load_tile(t + NWB, kB, vB);
+        load_tile_p(cpol, t + NWB, kB, vB);
         process(t, kA, vA);
-        load_tile(min(t + 2 * NWB, tlast), kA, vA);
+        load_tile_p(cpol, min(t + 2 * NWB, tlast), kA, vA);
         process(t + NWB, kB, vB);
       }
       if (i + 1 < nt) {
         const int t = tw + NWB * i;
-        load_tile(t + NWB, kB, vB);
+        load_tile_p(cpol, t + NWB, kB, vB);
         process(t, kA, vA);
         process(t + NWB, kB, vB);
       } else {
         process(tw + NWB * i, kA, vA);
       }
+    };
+    if (nt > 0) {
+      if (slice_is_pre(p, slice)) stream(kStream);
+      else stream(kKeep);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
