@@ -355,7 +355,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     float lsum = 0.f;
     const int t0 = ka / kTile, t1 = (ke + kTile - 1) / kTile;
 
-    auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
+    auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) __attribute__((always_inline)) {
       if (patcher && tt == tnew) {
         // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
         // (rows: V of token c, like K)
@@ -520,8 +520,10 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     // leave the caches to what is read again: the slices after p_new hold
     // the band and the tail, which the next steps read again whether they
     // hit or miss.  (Each policy has its own copy of the loop, chosen
-    // before it, so no load sits under a branch inside it.)
-    auto stream = [&](auto cpol) {
+    // before it, so no load sits under a branch inside it; fp32 d128 at
+    // two waves per SIMD has no registers for the second copy and streams
+    // every slice with the non-temporal policy.)
+    auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
       int i = 0;
@@ -541,9 +543,14 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
         process(tw + NWB * i, kA, vA);
       }
     };
+    constexpr bool kTwoLoops = !(sizeof(T) == 4 && D == 128 && NWV > 4);
     if (nt > 0) {
-      if (slice_is_pre(p, slice)) stream(kStream);
-      else stream(kKeep);
+      if constexpr (kTwoLoops) {
+        if (slice_is_pre(p, slice)) stream(kStream);
+        else stream(kKeep);
+      } else {
+        stream(kStream);
+      }
     }
     // slice 0 publishes the plan start for the second round of workgroups.
     // The store comes after the tile loop in program order (a global store

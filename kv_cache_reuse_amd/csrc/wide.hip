@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     }
     const int t0 = ka / kTile, t1 = (ke + kTile - 1) / kTile;
 
-    auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) {
+    auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) __attribute__((always_inline)) {
       if (patcher && tt == tnew) {
         // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
         // (rows: V of token c, like K)
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     // slices before p_new stream with the non-temporal policy, the band and
     // the tail (read again by the next steps) with the default one; one
     // copy of the loop per policy
-    auto stream = [&](auto cpol) {
+    auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
       int i = 0;
