@@ -522,7 +522,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     // hit or miss.  (Each policy has its own copy of the loop, chosen
     // before it, so no load sits under a branch inside it; fp32 d128 at
     // two waves per SIMD has no registers for the second copy and streams
-    // every slice with the non-temporal policy.)
+    // every slice with the non-temporal policy.  Natural rows keep the
+    // default: a row load covers half of each 128-byte line and the next
+    // load the other half, which a line not kept would fetch twice.)
     auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
@@ -545,7 +547,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     };
     constexpr bool kTwoLoops = !(sizeof(T) == 4 && D == 128 && NWV > 4);
     if (nt > 0) {
-      if constexpr (kTwoLoops) {
+      if constexpr (NAT) {
+        stream(kKeep);
+      } else if constexpr (kTwoLoops) {
         if (slice_is_pre(p, slice)) stream(kStream);
         else stream(kKeep);
       } else {

@@ -376,7 +376,8 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
     // slices before p_new stream with the non-temporal policy, the band and
     // the tail (read again by the next steps) with the default one; one
-    // copy of the loop per policy
+    // copy of the loop per policy (natural rows keep the default: a row
+    // load covers half of each 128-byte line, the next load the other half)
     auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
@@ -398,8 +399,12 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
       }
     };
     if (nt > 0) {
-      if (slice_is_pre(p, slice)) stream(kStream);
-      else stream(kKeep);
+      if constexpr (NAT) {
+        stream(kKeep);
+      } else {
+        if (slice_is_pre(p, slice)) stream(kStream);
+        else stream(kKeep);
+      }
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
