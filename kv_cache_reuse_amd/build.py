@@ -9,6 +9,7 @@ streaming-read probe the benchmark measures the bandwidth ceiling with.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBS = {
@@ -31,10 +32,7 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
-def _build_one(out: str, sources, verbose: bool) -> None:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = out + ".tmp"
-    cmd = [hipcc, *FLAGS, "-o", tmp, *[os.path.join(HERE, s) for s in sources]]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,6 +43,24 @@ def _build_one(out: str, sources, verbose: bool) -> None:
         raise RuntimeError(f"hipcc failed with status {r.returncode}")
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def _build_one(out: str, sources, verbose: bool) -> None:
+    """Each source compiles to an object of its own, in parallel, then one
+    link."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build", os.path.basename(out))
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in sources]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = [[hipcc, *compile_flags, "-c", "-o", o, os.path.join(HERE, s)]
+            for s, o in zip(sources, objs)]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, j, verbose) for j in jobs]:
+            f.result()
+    tmp = out + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
 
 
