@@ -13,7 +13,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBS = {
-    "libmac.so": ["csrc/step.hip", "csrc/wide.hip", "csrc/kv_ring.hip", "csrc/mac_api.hip"],
+    "libmac.so": ["csrc/step.hip", "csrc/merge.hip", "csrc/wide.hip", "csrc/kv_ring.hip",
+                  "csrc/mac_api.hip"],
     "libmac_bw.so": ["csrc/bw_probe.hip"],
 }
 SOURCES = LIBS["libmac.so"]

@@ -24,6 +24,10 @@ inline void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t st, hi
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1);
 
+// The merge launch of a step (merge.hip): log-sum-exp merge of each query
+// head's reused state and slices, its new ring entry and its output.
+hipError_t launch_merge(const StepArgs& a, int dtype, int d, hipStream_t st);
+
 // Wide groups (bf16, more than kMaxGroup heads per group): the match of
 // every query head (records, rotated queries, reused states) and the split-K
 // attention that reads them (wide.hip).

@@ -37,10 +37,9 @@
 //      p_new one wave loads the tile a typical hit starts in instead.  With a
 //      fused append, the workgroup whose slice holds the new token stores it
 //      in the cache and patches it into the tile it loads.
-//  merge_kernel, one workgroup per query head (one wave, or up to 16 for
-//  more than 32 slices): log-sum-exp merge of the reused state and the
-//  slices, the head's new ring entry and its output; with a fused append it
-//  also publishes the new length.
+//  The merge launch follows (merge.hip): per query head, the log-sum-exp
+//  merge of the reused state and the slices, the head's new ring entry and
+//  its output; with a fused append it also publishes the new length.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -646,247 +645,6 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   }
 }
 
-// ========================================================= merge kernel ==
-// Merge of one query head (b, h) by `nw` waves: log-sum-exp merge of the
-// reused state and the group's slices, the head's new ring entry and its
-// output.  Wave w takes the contiguous slices [k0, k1) of the group's S
-// (at most 64; lane j holds the (m, l) of slice k0 + j), and each lane owns
-// D/64 output dims.  A wave folds its slices' o in slice order, with each
-// side's (before and after p_new) weights taken relative to the wave's own
-// maximum; wave 0 then rescales and adds the waves' sums in wave order, so
-// results are bitwise reproducible, and with one wave the arithmetic is the
-// plain ordered fold.  The loads go out in one round (two for more than 32
-// slices per wave) and need nothing from the match records: the slices'
-// (m, l) first (loads complete in order, and the reductions need these
-// before any o), then the query the entry copies, the reused ring state as
-// the step kernel copied it for a hit head, and the slices' o (slices the
-// plan leaves unused hold stale values: read in bounds, never used).  The
-// records come through scalar loads alongside.
-constexpr int kMergeMaxWaves = 16;
-constexpr int kMergeBatch = 32;   // slices whose o one wave loads per round
-
-__host__ __device__ inline int merge_waves(int S) {
-  const int w = (S + kMergeBatch - 1) / kMergeBatch;
-  return w < kMergeMaxWaves ? w : kMergeMaxWaves;
-}
-
-template <int D>
-struct MergeShared {
-  float m[kMergeMaxWaves][2];           // per wave: max of the slices before / after p_new
-  float l[kMergeMaxWaves][2];
-  float o[kMergeMaxWaves][2][D];
-};
-
-template <typename T, int D, bool MW>
-__device__ __forceinline__ void merge_head(const StepArgs& a, int bh, int grp, int kvh, int hi,
-                                           int wave, int nw, int lane, MergeShared<MW ? D : 1>& xs) {
-  constexpr int DL = D / 64;            // output dims per lane
-  constexpr int kBatch = kMergeBatch;
-  const int b = bh / a.hq, h = bh % a.hq;
-  const int G = a.group, S = a.part.S;
-  const RingView& R = a.ring;
-  const size_t pbase = (size_t)grp * S * G + hi;        // slice k: pbase + k * G
-  const int spw = (S + nw - 1) / nw;
-  const int k0 = wave * spw;
-  const int k1 = k0 + spw < S ? k0 + spw : S;           // empty when k0 >= S
-
-  // ---- the loads
-  // the group's fresh-range starts, lane i < G holding head i's: one vector
-  // load, first (loads complete in order; a loop of scalar loads would wait
-  // for each record in turn)
-  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
-  const int s_lane = hsg[lane < G ? lane : 0].s;
-  const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
-  const int kl = k0 + lane < S ? k0 + lane : S - 1;
-  const float2 ml0 = pml[pbase + (size_t)kl * G];
-  const T* qsrc = static_cast<const T*>(a.q_pre) + (size_t)bh * D + DL * lane;
-  T qv[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) qv[e] = qsrc[e];
-  // the reused state (the ring stores natural-log m and normalized o), as
-  // the step kernel copied it for a hit head; stale otherwise, and then
-  // never selected
-  const float2 rml = reinterpret_cast<const float2*>(a.reuse_ml)[bh];
-  float ro[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) ro[e] = a.reuse_o[(size_t)bh * D + DL * lane + e];
-  float ob[kBatch][DL];
-  auto load_o = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int k = kb + u < S ? kb + u : S - 1;
-      const float* src = a.part.o + (pbase + (size_t)k * G) * D + DL * lane;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) ob[u][e] = src[e];
-    }
-  };
-  // wave 0 loads its slices' o in the first round: on a hit its slices are
-  // the only live ones.  The other waves' slices are live only when the
-  // plan is long (a miss); they load once the plan is known.
-  if (wave == 0) load_o(k0);
-  // the head's own record (uniform address: scalar loads) and the plan
-  const HeadState hs = hsg[hi];
-  const int lo = wave_min_i(s_lane);
-  const int n = hs.n;
-  const Plan p = make_plan(lo, n, a.band, S, a.part.first);
-  const int npart = p.n_pre + p.n_post;
-  const int ke = k1 < npart ? k1 : npart;               // this wave's live slices: [k0, ke)
-  if (MW && wave != 0 && k0 < ke) load_o(k0);
-
-  // ---- this wave's maxima of the slices before and after p_new, then
-  // weights relative to them (slice k0 + j's weight in lane j)
-  const bool live = k0 + lane < ke;
-  const bool pre0 = slice_is_pre(p, k0 + lane);
-  float mp = neg_inf(), mq = neg_inf();
-  if (live) {
-    if (pre0) mp = ml0.x;
-    else mq = ml0.x;
-  }
-  float MA = wave_max(mp), MC = wave_max(mq);
-  float lp = 0.f, lq = 0.f, w0 = 0.f;
-  if (live) {
-    w0 = ml0.x == neg_inf() ? 0.f : fast_exp2(ml0.x - (pre0 ? MA : MC));
-    if (pre0) lp += w0 * ml0.y;
-    else lq += w0 * ml0.y;
-  }
-  float LA = wave_sum(lp), LC = wave_sum(lq);
-
-  // ---- o of both sides (unnormalized, relative to MA and MC), slice order;
-  // weights read from the lane that holds them
-  float oa[DL], oc[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    if (k0 + u < ke) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
-      if (slice_is_pre(p, k0 + u)) {
-#pragma unroll
-        for (int e = 0; e < DL; ++e) oa[e] += w * ob[u][e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < DL; ++e) oc[e] += w * ob[u][e];
-      }
-    }
-  }
-  // a wave's second round (more than 32 slices per wave)
-  if (k0 + kBatch < ke) {
-    load_o(k0 + kBatch);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (k0 + kBatch + u < ke) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), kBatch + u));
-        if (slice_is_pre(p, k0 + kBatch + u)) {
-#pragma unroll
-          for (int e = 0; e < DL; ++e) oa[e] += w * ob[u][e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < DL; ++e) oc[e] += w * ob[u][e];
-        }
-      }
-    }
-  }
-
-  // ---- the waves' sums, rescaled to the largest maximum and added in wave
-  // order by wave 0
-  if constexpr (MW) {
-    if (lane == 0) {
-      xs.m[wave][0] = MA;
-      xs.m[wave][1] = MC;
-      xs.l[wave][0] = LA;
-      xs.l[wave][1] = LC;
-    }
-#pragma unroll
-    for (int e = 0; e < DL; ++e) {
-      xs.o[wave][0][DL * lane + e] = oa[e];
-      xs.o[wave][1][DL * lane + e] = oc[e];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    MA = xs.m[0][0];
-    MC = xs.m[0][1];
-    for (int w = 1; w < nw; ++w) {
-      MA = fmaxf(MA, xs.m[w][0]);
-      MC = fmaxf(MC, xs.m[w][1]);
-    }
-    LA = LC = 0.f;
-#pragma unroll
-    for (int e = 0; e < DL; ++e) oa[e] = oc[e] = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float ma = xs.m[w][0], mc = xs.m[w][1];
-      const float sa = ma == neg_inf() ? 0.f : fast_exp2(ma - MA);
-      const float sc = mc == neg_inf() ? 0.f : fast_exp2(mc - MC);
-      LA += sa * xs.l[w][0];
-      LC += sc * xs.l[w][1];
-#pragma unroll
-      for (int e = 0; e < DL; ++e) {
-        oa[e] += sa * xs.o[w][0][DL * lane + e];
-        oc[e] += sc * xs.o[w][1][DL * lane + e];
-      }
-    }
-  }
-
-  // ---- prefix = merge(reused, A), base 2
-  const float mr = (hs.hit && rml.x != neg_inf()) ? rml.x * static_cast<float>(kLog2e) : neg_inf();
-  const float lr = hs.hit ? rml.y : 0.f;
-  const float MP = fmaxf(mr, MA);
-  const float sr = mr == neg_inf() ? 0.f : fast_exp2(mr - MP);
-  const float sa = MA == neg_inf() ? 0.f : fast_exp2(MA - MP);
-  const float LP = sr * lr + sa * LA;
-  const float fr = sr * lr;
-  float po[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) po[e] = hs.hit ? fr * ro[e] + sa * oa[e] : sa * oa[e];
-
-  // ---- the head's new ring entry: (q_pre, prefix state, p_new, n)
-  const size_t we = (size_t)bh * R.slots + hs.cnt % R.slots;
-  T* qdst = static_cast<T*>(R.q) + we * D + DL * lane;
-#pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    R.o[we * D + DL * lane + e] = LP == 0.f ? 0.f : po[e] / LP;
-    qdst[e] = qv[e];
-  }
-
-  // ---- out = merge(prefix, C)
-  const float M = fmaxf(MP, MC);
-  const float sp = MP == neg_inf() ? 0.f : fast_exp2(MP - M);
-  const float sc = MC == neg_inf() ? 0.f : fast_exp2(MC - M);
-  const float den = sp * LP + sc * LC;
-#pragma unroll
-  for (int e = 0; e < DL; ++e)
-    a.out[(size_t)bh * D + DL * lane + e] = den == 0.f ? 0.f : (sp * po[e] + sc * oc[e]) / den;
-  if (lane == 0) {
-    R.ml[we * 2] = LP == 0.f ? neg_inf() : MP * kLn2;
-    R.ml[we * 2 + 1] = LP;
-    R.pn[we * 2] = p.mid;
-    R.pn[we * 2 + 1] = n;
-    R.count[bh] = hs.cnt + 1;
-    // fused append: publish the new length (no kernel of this step reads it
-    // after the step kernel)
-    if (a.k_new && h == 0) a.seq_lens[b] = n;
-    // the group's published plan start is spent: clear it, so that every
-    // step begins with no plan published and no later step (of this context
-    // or of another one the workspace serves next) can take this one
-    if (hi == 0 && a.part.first < a.part.S) a.plan_pub[grp] = ~0ull;
-  }
-}
-
-// One workgroup of merge_waves(S) waves per query head, a launch after the
-// step kernel: the group's match results come from the step kernel's records.
-// MW: more than one wave (a separate instantiation, so the one-wave merge
-// keeps a one-wave register budget and has no exchange).
-template <typename T, int D, bool MW>
-__global__ __launch_bounds__(MW ? 64 * kMergeMaxWaves : 64) void merge_kernel(StepArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.hq, h = bh % a.hq;
-  const int G = a.group, kvh = h / G, hi = h % G;
-  const int grp = b * a.hkv + kvh;
-  const int wave = MW ? __builtin_amdgcn_readfirstlane(threadIdx.x / 64) : 0;
-  const int nw = MW ? blockDim.x / 64 : 1;
-  __shared__ MergeShared<MW ? D : 1> xs;
-  merge_head<T, D, MW>(a, bh, grp, kvh, hi, wave, nw, threadIdx.x % 64, xs);
-}
-
 hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1) {
   if (a.group > kMaxGroup) {
@@ -923,14 +681,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
     }
 #undef L_STEP
 #undef L_STEP_L
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-#define L_MERGE(T, D)                                                                              \
-  if (merge_waves(a.part.S) > 1)                                                                   \
-    hipLaunchKernelGGL((merge_kernel<T, D, true>), dim3(a.batch * a.hq), dim3(64 * merge_waves(a.part.S)), 0, st, a); \
-  else hipLaunchKernelGGL((merge_kernel<T, D, false>), dim3(a.batch * a.hq), dim3(64), 0, st, a)
-  MAC_DISPATCH(dtype, d, L_MERGE);
-#undef L_MERGE
-  return hipGetLastError();
+  return launch_merge(a, dtype, d, st);
 }
 
 }  // namespace mac

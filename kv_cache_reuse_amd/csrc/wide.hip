@@ -23,7 +23,7 @@
 //  head.  With a fused append, the workgroup whose slice holds the new token
 //  stores it in the cache and patches it into the tile it loads.
 //
-//  merge_kernel (step.hip) folds the partial states as for narrow groups.
+//  the merge launch (merge.hip) folds the partial states as for narrow groups.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
