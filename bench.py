@@ -24,7 +24,9 @@ per-step p10/p50/p90 at jump probability 0.2 split by the step's decisions
 (8B shape at 32K keys, the ragged paged batch of 8, the 70B shape and its
 rho-per-KV-head supplement): miss path with the step kernel's achieved
 bandwidth, the workload's own stream and the all-hit step; `seeding` the
-cost of seeding the rings from the prefill (1 and W positions); `drift` the
+cost of seeding the rings from the prefill (1 and W positions); `calls`
+the miss and all-hit steps as two calls (mac_append_kv, mac_decode_step)
+against the fused call, and mac_append_kv alone; `drift` the
 largest |out_MAC - out_dense| on a 16K continuous-generation stream by
 reuse-chain depth, over tau and B; `multilayer` every layer of a token in
 one graph (32 layers, 16K keys); `mqa` 32 query heads over one KV head at
@@ -138,16 +140,33 @@ class Layer:
             n = self.ctx[b] if upto is None else upto
             self.sess.prefill(b, self.K[b, :, :n], self.V[b, :, :n])
 
-    def step(self, stream=None):
+    def step(self, stream=None, separate=False):
         from kv_cache_reuse_amd import binding as B
         t = self.t
         s = self.sess
         st = s._s() if stream is None else stream
-        # append + match + split-K attention + merge: one library call
-        B.mac_decode_step_append(s.ctx, self.q[t].data_ptr(), self.k_new[t].data_ptr(),
-                                 self.v_new[t].data_ptr(), s.k_cache.data_ptr(),
-                                 s.v_cache.data_ptr(), s._pt(), self.out[t].data_ptr(),
-                                 self.match_n[t].data_ptr(), 0, st)
+        if separate:
+            # mac_append_kv, then mac_decode_step: two library calls
+            B.mac_append_kv(s.ctx, s.k_cache.data_ptr(), s.v_cache.data_ptr(), s._pt(),
+                            self.k_new[t].data_ptr(), self.v_new[t].data_ptr(), st)
+            B.mac_decode_step(s.ctx, self.q[t].data_ptr(), s.k_cache.data_ptr(),
+                              s.v_cache.data_ptr(), s._pt(), self.out[t].data_ptr(),
+                              self.match_n[t].data_ptr(), 0, st)
+        else:
+            # append + match + split-K attention + merge: one library call
+            B.mac_decode_step_append(s.ctx, self.q[t].data_ptr(), self.k_new[t].data_ptr(),
+                                     self.v_new[t].data_ptr(), s.k_cache.data_ptr(),
+                                     s.v_cache.data_ptr(), s._pt(), self.out[t].data_ptr(),
+                                     self.match_n[t].data_ptr(), 0, st)
+        self.t += 1
+
+    def append_only(self, stream):
+        """mac_append_kv of the next token alone (no decode)."""
+        from kv_cache_reuse_amd import binding as B
+        t = self.t
+        s = self.sess
+        B.mac_append_kv(s.ctx, s.k_cache.data_ptr(), s.v_cache.data_ptr(), s._pt(),
+                        self.k_new[t].data_ptr(), self.v_new[t].data_ptr(), stream)
         self.t += 1
 
 
@@ -216,7 +235,7 @@ def layer_jump_schedules(p, steps, warmup, layers, per_layer):
 
 def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
               context=None, prefill_upto=None, inputs_cache=None, per_step=False,
-              seeded=False, kv_layout=0):
+              seeded=False, kv_layout=0, separate=False):
     """warmup + steps decode steps, round-robin over `layers` layer copies.
 
     The warmup runs eagerly.  With `graph` the timed steps are captured into
@@ -237,7 +256,7 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     torch.cuda.synchronize()
     order = [i % layers for i in range(warmup + steps)]
     for i in order[:warmup]:
-        Ls[i].step()
+        Ls[i].step(separate=separate)
     torch.cuda.synchronize()
     starts = [L.t for L in Ls]
     use_graph = graph and not kernel_timing and not per_step
@@ -247,7 +266,7 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
             for i in order[warmup:]:
-                Ls[i].step(stream=cs)
+                Ls[i].step(stream=cs, separate=separate)
         torch.cuda.synchronize()
     if kernel_timing:
         for L in Ls:
@@ -265,11 +284,11 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
                 ea = torch.cuda.Event(enable_timing=True)
                 eb = torch.cuda.Event(enable_timing=True)
                 ea.record(stream)
-                Ls[i].step()
+                Ls[i].step(separate=separate)
                 eb.record(stream)
                 marks.append((i, Ls[i].t - 1, ea, eb))
             else:
-                Ls[i].step()
+                Ls[i].step(separate=separate)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -761,6 +780,7 @@ def main():
     ap.add_argument("--no-c2", action="store_true")
     ap.add_argument("--no-c5", action="store_true")
     ap.add_argument("--no-layout", action="store_true")
+    ap.add_argument("--no-calls", action="store_true")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -853,6 +873,29 @@ def main():
         log(f"layout A/B: step kernel tiles {kern_sec * 1e6:.1f} us, rows {us_r:.1f} us; all-hit "
             f"step tiles {layout_ab['tiles_all_hit_us_per_step']:.2f} us, rows "
             f"{layout_ab['rows_all_hit_us_per_step']:.2f} us")
+
+    # ---- mac_append_kv and mac_decode_step as two calls against the fused
+    # call, and mac_append_kv alone
+    calls = None
+    if not args.no_calls:
+        ms_s, rec_s, _, _ = run_point(w, 1.0, args.steps, args.warmup, args.layers,
+                                      inputs_cache=cache, seeded=True, separate=True)
+        msh_s, rh_s, _, _ = run_point(w, 0.0, args.steps, args.warmup, args.layers,
+                                      inputs_cache=cache, seeded=True, separate=True)
+        msh_f, rh_f, _, _ = run_point(w, 0.0, args.steps, args.warmup, args.layers,
+                                      inputs_cache=cache, seeded=True)
+        k_app, us_app = append_alone(w, args.steps, args.warmup, args.layers, cache)
+        calls = {"workload": "8b_128k: miss path and all-hit step, graph-replayed; "
+                             "mac_append_kv alone over the same layer copy",
+                 "fused_miss_us_per_token": head["us_per_token"],
+                 "separate_miss_us_per_token": summarize(w, ms_s, rec_s, args.steps)["us_per_token"],
+                 "fused_all_hit_us_per_step": summarize(w, msh_f, rh_f, args.steps)["us_per_step"],
+                 "separate_all_hit_us_per_step": summarize(w, msh_s, rh_s, args.steps)["us_per_step"],
+                 "append_us": us_app, "append_calls": k_app}
+        log(f"calls: miss step fused {calls['fused_miss_us_per_token']:.2f} / separate "
+            f"{calls['separate_miss_us_per_token']:.2f} us; all-hit fused "
+            f"{calls['fused_all_hit_us_per_step']:.2f} / separate "
+            f"{calls['separate_all_hit_us_per_step']:.2f} us; mac_append_kv alone {us_app:.2f} us")
 
     # ---- hit-rate sweep
     sweep = []
@@ -977,11 +1020,40 @@ def main():
         "mqa": mq,
         "configs": configs,
         "layout_ab": layout_ab,
+        "calls": calls,
         "read_ceiling": ceil,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def append_alone(w, steps, warmup, layers, cache):
+    """mac_append_kv alone: the calls a layer copy of the headline point can
+    take (its decode-step inputs), captured in one HIP graph and replayed
+    once.  Returns (calls, us per call)."""
+    import torch
+    per_layer = (steps + warmup + layers - 1) // layers + 1
+    L = make_layers(w, 1.0, per_layer, 1, cache)[0]
+    k = per_layer - 1
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(k):
+            L.append_only(cs)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / k
+    del g
+    L.sess.close()
+    return k, us
 
 
 def hit_step_latency(w, cache, steps=128):
