@@ -313,21 +313,41 @@ def run_point(w, p_jump, steps, warmup, layers, kernel_timing=False, graph=True,
     classes = [(("all_hit" if (mns[i][t] >= 0).all() else
                  "all_miss" if (mns[i][t] < 0).all() else "mixed"), us)
                for i, t, us in step_us]
+    # one record per timed step (per_step): decisions, bytes and time
+    steplog = []
+    for (i, t, us), (cls, _) in zip(step_us, classes):
+        mn = mns[i][t]
+        n_ctx = Ls[i].inp.contexts + t + 1
+        cnt = np.full((w.batch, w.n_q_heads), min(t + hist, w.window))
+        tot, _, keys = step_bytes(w, n_ctx, mn, cnt)
+        g = (mn >= 0).reshape(w.batch, w.n_kv_heads, w.group).all(axis=2)
+        steplog.append({"layer": int(i), "step": int(t), "n": [int(x) for x in n_ctx],
+                        "class": cls, "us": float(us), "hit_rate": float((mn >= 0).mean()),
+                        "group_all_hit": float(g.mean()), "matched_n": mn.tolist(),
+                        "kv_keys": int(keys), "bytes": int(tot)})
     del g
     for L in Ls:
         L.sess.close()
     del Ls
     torch.cuda.empty_cache()
     if per_step:
-        return ms, recs, kms, klaunch, classes
+        return ms, recs, kms, klaunch, classes, steplog
     return ms, recs, kms, klaunch
 
 
-def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache, seeded=False):
+def latency_classes(w, p_jump, steps, warmup, layers, inputs_cache, seeded=False, log_path=None):
     """Per-step latency (HIP events around each eager step) by the step's
-    decisions: every head hit, every head missed, or mixed."""
+    decisions: every head hit, every head missed, or mixed.  With log_path,
+    one JSON line per timed step is appended there (workload, layer copy,
+    step, context lengths, decision class, µs, head and group hit rates, the
+    matched context length of every head (-1 on a miss), KV keys read and
+    algorithmic bytes)."""
     out = run_point(w, p_jump, steps, warmup, layers, graph=False, inputs_cache=inputs_cache,
                     per_step=True, seeded=seeded)
+    if log_path:
+        with open(log_path, "a") as fh:
+            for rec in out[5]:
+                fh.write(json.dumps({"workload": w.name, "p_jump": p_jump, **rec}) + "\n")
     res = {}
     for cls in ("all_hit", "mixed", "all_miss"):
         v = np.array([us for c, us in out[4] if c == cls])
@@ -538,7 +558,8 @@ CONFIG_POINTS = {
 }
 
 
-def config_point(key, steps, warmup, cache, miss=True, classes=False, streams=True):
+def config_point(key, steps, warmup, cache, miss=True, classes=False, streams=True,
+                 log_path=None):
     """One workload of the configs: its miss path (every token jumps), graph-
     replayed, with the step kernel timed by HIP events in an eager run (that
     kernel's roofline at this shape); its own query stream (its jump
@@ -575,7 +596,7 @@ def config_point(key, steps, warmup, cache, miss=True, classes=False, streams=Tr
             f"all-hit {sp['group_all_hit']:.3f}, dense-equivalent {sp['dense_equiv_GBps']:.0f} GB/s)")
     if classes:
         res["latency_classes"] = latency_classes(w, w.p_jump, steps, warmup, layers, cache,
-                                                 seeded=True)
+                                                 seeded=True, log_path=log_path)
         for k, v in res["latency_classes"].items():
             log(f"  {key} {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / "
                 f"{v['p50_us']:.1f} / {v['p90_us']:.1f} us")
@@ -781,6 +802,8 @@ def main():
     ap.add_argument("--no-c5", action="store_true")
     ap.add_argument("--no-layout", action="store_true")
     ap.add_argument("--no-calls", action="store_true")
+    ap.add_argument("--step-log", type=str, default="",
+                    help="append one JSON line per timed step of the latency-class runs here")
     ap.add_argument("--drift-steps", type=int, default=2048)
     ap.add_argument("--cpu-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
@@ -928,7 +951,8 @@ def main():
     lat = None
     if not args.no_latency:
         log("latency classes: p_jump=0.2, eager per-step events")
-        lat = latency_classes(w, 0.2, args.steps, args.warmup, args.layers, cache, seeded=True)
+        lat = latency_classes(w, 0.2, args.steps, args.warmup, args.layers, cache, seeded=True,
+                              log_path=args.step_log or None)
         for k, v in lat.items():
             log(f"  {k}: {v['steps']} steps, p10/p50/p90 {v['p10_us']:.1f} / {v['p50_us']:.1f} / "
                 f"{v['p90_us']:.1f} us")
@@ -960,7 +984,8 @@ def main():
         log(f"config point {key}")
         configs[key] = config_point(key, min(args.steps, 64), min(args.warmup, 8),
                                     cache if key != "paged_b8" else {},
-                                    miss=key != "70b_128k_rho_per_kv", classes=key == "8b_32k")
+                                    miss=key != "70b_128k_rho_per_kv", classes=key == "8b_32k",
+                                    log_path=args.step_log or None)
         if key.startswith("70b"):
             cache = {k: v for k, v in cache.items() if not k[0].startswith("70b")}
 
