@@ -54,10 +54,16 @@ template <typename T, int D, int MD, int PER>
 __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(StepArgs a) {
   constexpr int QP = D / MD;                    // workgroups per query head
   constexpr int NP = 64 / MD;                   // parts of a wave
-  const int bh = blockIdx.x / QP, q = blockIdx.x % QP;
-  const int b = bh / a.hq, h = bh % a.hq;
-  const int G = a.group, kvh = h / G, hi = h % G;
-  const int grp = b * a.hkv + kvh;
+  // ids run group-major: id mod groups is the KV group, so (with a multiple
+  // of 8 groups) a group's merge workgroups share the XCD its step
+  // workgroups ran on, whose L2 holds the partial states they wrote
+  const int groups = a.batch * a.hkv;
+  const int grp = blockIdx.x % groups, rest = blockIdx.x / groups;
+  const int q = rest % QP, hi = rest / QP;
+  const int G = a.group;
+  const int b = grp / a.hkv, kvh = grp % a.hkv;
+  const int h = kvh * G + hi;
+  const int bh = b * a.hq + h;
   const int S = a.part.S;
   const int nw = blockDim.x / 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
