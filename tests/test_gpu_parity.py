@@ -267,7 +267,7 @@ def test_nan_query_poisons_only_its_head():
 # ---------------------------------------------------------------------------
 
 FULL = {
-    # name: (workload, overrides, decode steps)
+    # name: (workload, overrides, decode steps[, run_gpu options])
     "8b_32k": ("8b_32k", dict(), 256),
     "8b_128k_p1": ("8b_128k", dict(p_jump=1.0), 512),
     "8b_128k_p05": ("8b_128k", dict(p_jump=0.5), 512),
@@ -279,17 +279,20 @@ FULL = {
     # heads), so that whole groups hit and take the band-and-tail path
     "70b_128k_rho_per_kv": ("70b_128k", dict(rho_per_kv=True), 256),
     "8b_128k_mqa": ("8b_128k", dict(n_kv_heads=1, p_jump=0.2), 48),
+    # natural-row caches (kv_layout 1) in the same launch configuration
+    "8b_32k_rows": ("8b_32k", dict(), 256, dict(kv_layout=1)),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_every_group(name):
-    base, kw, steps = FULL[name]
+    base, kw, steps, *opts = FULL[name]
+    opts = opts[0] if opts else {}
     w = workload(base, **kw, steps=steps)
     say(f"[full:{name}] generating {w}")
     inp = make_inputs(w)
-    say(f"[full:{name}] gpu run, {steps} steps")
-    gpu = run_gpu(w, inp, fused=True)
+    say(f"[full:{name}] gpu run, {steps} steps {opts}")
+    gpu = run_gpu(w, inp, fused=True, **opts)
     groups = all_groups(w)
     say(f"[full:{name}] oracle replay of {len(groups)} KV groups x {steps} steps")
 
