@@ -28,6 +28,7 @@
 #include "mac_dev.h"
 #include "mac_launch.h"
 #include "match.h"
+#include "merge_map.h"
 
 namespace mac {
 
@@ -54,15 +55,12 @@ template <typename T, int D, int MD, int PER>
 __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(StepArgs a) {
   constexpr int QP = D / MD;                    // workgroups per query head
   constexpr int NP = 64 / MD;                   // parts of a wave
-  // ids run group-major: id mod groups is the KV group, so (with a multiple
-  // of 8 groups) a group's merge workgroups share the XCD its step
-  // workgroups ran on, whose L2 holds the partial states they wrote
-  const int groups = a.batch * a.hkv;
-  const int grp = blockIdx.x % groups, rest = blockIdx.x / groups;
-  const int q = rest % QP, hi = rest / QP;
+  // ids run group-major (merge_coords): with a multiple of 8 groups a
+  // group's merge workgroups share the XCD its step workgroups ran on,
+  // whose L2 holds the partial states they wrote
+  const MergeCoords mc = merge_coords(blockIdx.x, a.batch, a.hkv, a.group, QP);
+  const int grp = mc.grp, b = mc.b, h = mc.h, hi = mc.hi, q = mc.q;
   const int G = a.group;
-  const int b = grp / a.hkv, kvh = grp % a.hkv;
-  const int h = kvh * G + hi;
   const int bh = b * a.hq + h;
   const int S = a.part.S;
   const int nw = blockDim.x / 64;
@@ -81,7 +79,7 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void merge_kernel(StepArgs a) 
   // ---- the loads, one round: the group's starts (lane i < G: head i's;
   // one vector load), this lane's slices' (m, l) and o, the query the entry
   // copies, and the reused state as the step (or match) kernel copied it
-  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)kvh * G;
+  const HeadState* hsg = a.heads + (size_t)b * a.hq + (size_t)(h - hi);
   const int s_lane = hsg[lane < G ? lane : 0].s;
   const float2* pml = reinterpret_cast<const float2*>(a.part.ml);
   float2 ml[PER];

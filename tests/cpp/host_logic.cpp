@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "../../kv_cache_reuse_amd/csrc/mac_dev.h"
+#include "../../kv_cache_reuse_amd/csrc/merge_map.h"
 
 static int fails = 0;
 #define CHECK(c, ...)                         \
@@ -144,6 +145,30 @@ void check_coords(int groups, int nchunk, int S, int hkv = 1, int first = 0,
       }
 }
 
+// Every (query head, dim part) of the merge launch gets exactly one id, the
+// head's group is the one it belongs to, and with a multiple of 8 groups
+// every merge workgroup of a group is on the XCD of the group's step
+// workgroups (ids congruent mod 8 to the group's step ids).
+void check_merge_coords(int batch, int hkv, int group, int parts, int S) {
+  const int hq = hkv * group, n = batch * hq * parts, groups = batch * hkv;
+  std::vector<int> seen((size_t)n, 0);
+  for (int id = 0; id < n; ++id) {
+    const mac::MergeCoords m = mac::merge_coords(id, batch, hkv, group, parts);
+    const bool ok = m.b >= 0 && m.b < batch && m.h >= 0 && m.h < hq && m.q >= 0 && m.q < parts &&
+                    m.hi == m.h % group && m.grp == m.b * hkv + m.h / group;
+    CHECK(ok, "merge id %d -> (b %d, h %d, hi %d, q %d, grp %d)", id, m.b, m.h, m.hi, m.q, m.grp);
+    if (!ok) continue;
+    seen[((size_t)m.b * hq + m.h) * parts + m.q]++;
+    if (groups % mac::kXcds == 0) {
+      int g = -1, s = -1;
+      mac::step_coords(m.grp + groups * (S - 1), groups, 1, S, &g, &s);
+      CHECK(g == m.grp && id % mac::kXcds == (m.grp + groups * (S - 1)) % mac::kXcds,
+            "merge id %d of group %d on another XCD", id, m.grp);
+    }
+  }
+  for (int i = 0; i < n; ++i) CHECK(seen[i] == 1, "merge (head, part) %d taken %d times", i, seen[i]);
+}
+
 int main() {
   check_tiles<uint16_t>(64);
   check_tiles<uint16_t>(128);
@@ -163,6 +188,10 @@ int main() {
   }
   for (int groups : {1, 2, 3, 8, 16, 64})
     for (int S : {2, 5, 32, 128, 1024}) check_coords(groups, 1, S);
+  for (int batch : {1, 2, 3, 8})
+    for (int hkv : {1, 2, 8})
+      for (int group : {1, 4, 8, 16, 32})
+        for (int parts : {4, 8}) check_merge_coords(batch, hkv, group, parts, 32);
   // second-round orders: batch x hkv groups, first < S, random permutations
   std::mt19937 orng(7);
   for (int batch : {2, 3, 8, 11, 16})
