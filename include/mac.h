@@ -102,7 +102,7 @@ typedef struct {
   float tau;                 /* >= 0; hit iff dist < tau (fp32 dist^2 test)  */
   double rope_theta;         /* > 0                                          */
   int32_t max_slices;        /* split-K slices per KV group; 0 = default     */
-  int32_t kv_layout;         /* mac_kv_layout; MAC_KV_ROWS needs bf16        */
+  int32_t kv_layout;         /* mac_kv_layout                                */
 } mac_config;
 
 /*
@@ -132,7 +132,7 @@ typedef struct mac_ctx mac_ctx;
  * KV cache layouts (abstract: the method "composes with ... paged-KV
  * managers"; a cache is contiguous or paged, in 16-token pages).
  *
- * MAC_KV_ROWS, natural rows (bf16 only): element (b, g, pos, i) of a
+ * MAC_KV_ROWS, natural rows (either dtype): element (b, g, pos, i) of a
  *   contiguous cache is at ((b*Hkv + g)*max_context + pos)*d + i, the layout
  *   [batch][Hkv][max_context][d]; in a paged cache (page_size 16) position
  *   pos of sequence b is row pos % 16 of page page_table[b*max_pages_per_seq

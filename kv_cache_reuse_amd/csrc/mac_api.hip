@@ -133,8 +133,6 @@ mac_status check_config(const mac_config* c) {
   if (c->kv_layout != MAC_KV_TILES && c->kv_layout != MAC_KV_ROWS)
     return fail(MAC_ERR_INVALID_ARG, "kv_layout must be MAC_KV_TILES or MAC_KV_ROWS (got %d)",
                 c->kv_layout);
-  if (c->kv_layout == MAC_KV_ROWS && c->dtype != MAC_DTYPE_BF16)
-    return fail(MAC_ERR_UNSUPPORTED, "the row (natural) KV layout is built for bf16 caches only");
   if (c->page_size == 0) {
     if (c->max_context < 1)
       return fail(MAC_ERR_INVALID_ARG, "max_context must be >= 1 (got %d)", c->max_context);

@@ -26,10 +26,10 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // ------------------------------------------------- natural-layout values --
 // Value tiles in the natural (row) layout arrive with lane (lg, c) holding
-// token c, bf16 elements [8 (4 j + lg), +8) of block j: the order of the key
+// token c, elements [E (4 j + lg), +E) of block j: the order of the key
 // operand, not of the value operand.  The wave writes the tile to LDS rows of
-// its own (ROWS = 16 rows of D + 8 elements; 16-byte aligned) and reads it
-// back in the value operand order of the library's tiles: vr[i] holds tokens
+// its own and reads it back in the value operand order of the library's
+// tiles.  bf16 (16 rows of D + 8 elements; 16-byte aligned): vr[i] holds tokens
 // 4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element 4 th + r,
 // two per dword).  LDS accesses of one wave complete in order, so the reads
 // see the writes, and a later tile's writes follow this tile's reads.
@@ -38,6 +38,32 @@ struct VRows {
   static constexpr int RS = D + 8;
   __attribute__((aligned(16))) uint16_t v[16 * RS];
 };
+
+// fp32 values: lane (lg, c) holds token c, elements [4 (4 j + lg), +4) of
+// block j (D / 16 blocks); rows of D + 4 floats (16-byte aligned; the reads
+// of one element of 64 lanes then fall in 64 different banks), read back
+// as vr[i] = tokens 4 lg .. 4 lg + 3 of dim 16 i + c, the value operand
+// order of the library's fp32 tiles.
+template <int D>
+struct VRowsF {
+  static constexpr int RS = D + 4;
+  __attribute__((aligned(16))) float v[16 * RS];
+};
+
+template <int D>
+__device__ __forceinline__ void v_rows_to_operand(VRowsF<D>& rows, int lane, u4 (&vr)[D / 16]) {
+  constexpr int NL = D / 16;
+  constexpr int RS = VRowsF<D>::RS;
+  const int lg = lane / 16, c = lane % 16;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) *reinterpret_cast<u4*>(rows.v + c * RS + 4 * (4 * j + lg)) = vr[j];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int d = 16 * i + c;
+    vr[i] = u4{__float_as_uint(rows.v[(4 * lg + 0) * RS + d]), __float_as_uint(rows.v[(4 * lg + 1) * RS + d]),
+               __float_as_uint(rows.v[(4 * lg + 2) * RS + d]), __float_as_uint(rows.v[(4 * lg + 3) * RS + d])};
+  }
+}
 
 template <int D>
 __device__ __forceinline__ void v_rows_to_operand(VRows<D>& rows, int lane, u4 (&vr)[D / 32]) {

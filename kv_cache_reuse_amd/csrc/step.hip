@@ -89,7 +89,7 @@ __host__ __device__ constexpr int step_waves() {
 // group than one round fills): the slice-0 workgroup publishes its plan
 // start and second-round workgroups whose slice is empty leave early.  A
 // separate instantiation, so that one-round launches carry none of it.
-// NAT: caches in the natural (row) layout (bf16 only): keys load with row
+// NAT: caches in the natural (row) layout: keys load with row
 // offsets, and each value tile passes through the wave's LDS rows into the
 // value operand order.
 template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false, bool NAT = false>
@@ -105,8 +105,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
   __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
-  static_assert(!NAT || BF, "the row layout is built for bf16 caches");
-  __shared__ VRows<NAT ? D : 32> vrows[NAT ? NWB : 1];
+  // natural rows: each streaming wave's LDS rows for its value tiles
+  using VR = std::conditional_t<BF, VRows<NAT ? D : 32>, VRowsF<NAT ? D : 32>>;
+  __shared__ VR vrows[NAT ? NWB : 1];
   // (padding ids of a chunked group get slice S: no plan gives it work, and
   // it writes nothing; no early return here, so that the compiler issues the
   // argument loads phase A needs together with the ones for this mapping)
@@ -674,8 +675,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d, int paged, hipStream
     launch_attention(step_kernel<T, D, false, false, true, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a); \
   else launch_attention(step_kernel<T, D, false, false, false, NAT>, dim3(grid), dim3(64 * step_waves<T, D, false>()), st, ev0, ev1, a)
 #define L_STEP(T, D) L_STEP_L(T, D, false)
-    if (a.geom.natural) {   // rows: bf16 only
-      if (d == 128) { L_STEP_L(uint16_t, 128, true); } else { L_STEP_L(uint16_t, 64, true); }
+    if (a.geom.natural) {
+#define L_STEP_N(T, D) L_STEP_L(T, D, true)
+      MAC_DISPATCH(dtype, d, L_STEP_N);
+#undef L_STEP_N
     } else {
       MAC_DISPATCH(dtype, d, L_STEP);
     }

@@ -47,7 +47,7 @@ BAD = [
     # a group must split into equal parts of at most 32 heads (bf16) or 16 (fp32)
     (dict(n_q_heads=8 * 33), 2), (dict(n_q_heads=8 * 17, dtype=0), 2),
     (dict(head_dim=96), 2), (dict(dtype=7), 2),
-    (dict(kv_layout=2), 1), (dict(kv_layout=1, dtype=0), 2),
+    (dict(kv_layout=2), 1),
     (dict(window=-1), 1), (dict(band=-3), 1), (dict(tau=-1.0), 1),
     (dict(tau=float("nan")), 1), (dict(rope_theta=0.0), 1),
     (dict(rope_theta=float("inf")), 1), (dict(max_slices=1), 1),
@@ -96,6 +96,9 @@ def test_sizes_of_a_valid_config(B):
     paged_rows = valid_cfg(B, page_size=16, max_pages_per_seq=300, n_pages=1000,
                            kv_layout=B.MAC_KV_ROWS)
     assert B.mac_kv_cache_bytes(paged_rows) == B.mac_kv_cache_bytes(paged)
+    # fp32 rows too
+    rows32 = valid_cfg(B, kv_layout=B.MAC_KV_ROWS, max_context=4097, dtype=B.MAC_DTYPE_F32)
+    assert B.mac_kv_cache_bytes(rows32) == 8 * 4097 * 128 * 4
 
 
 @pytest.mark.parametrize("name,capacity,slices", [

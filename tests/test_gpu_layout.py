@@ -2,6 +2,8 @@
 tile layout, bitwise, for every kernel variant, and caches written directly
 by the caller (needs an MI355X)."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,18 @@ CASES = {
     "mqa_g64_paged": ("paged_b8", dict(batch=2, n_q_heads=64, n_kv_heads=1, ctx_range=(500, 1200),
                                        steps=12), {}),
     "d64": ("8b_32k", dict(head_dim=64, context=1500, steps=16, tau=4.0), {}),
+    # fp32 caches: every fp32 instantiation of the step kernel
+    "f32_d128": ("tiny", dict(head_dim=128, n_q_heads=8, n_kv_heads=2, context=900, steps=16,
+                              tau=0.5 * math.sqrt(128)), {}),
+    "f32_d128_g8": ("tiny", dict(head_dim=128, n_q_heads=16, n_kv_heads=2, context=1100,
+                                 steps=12, tau=0.5 * math.sqrt(128)), {}),
+    "f32_d64_mqa": ("tiny", dict(n_q_heads=32, n_kv_heads=1, context=1300, steps=12), {}),
+    "f32_d64_paged": ("paged_b8", dict(dtype="f32", head_dim=64, batch=2, ctx_range=(400, 1100),
+                                       steps=12, tau=0.5 * math.sqrt(64)), {}),
+    "f32_paged_g8": ("paged_b8", dict(dtype="f32", batch=2, n_q_heads=32, n_kv_heads=4,
+                                      ctx_range=(300, 900), steps=12), {}),
+    "f32_rounds": ("paged_b8", dict(dtype="f32", page_size=0, ctx_range=(700, 1500), steps=12,
+                                    p_jump=0.15), dict(capacity=30000)),
 }
 
 
@@ -56,7 +70,7 @@ def test_rows_equal_tiles_bitwise(name):
 
 
 @pytest.mark.parametrize("name", ["narrow", "narrow_ragged_capacity", "paged", "paged_rounds",
-                                  "mqa_g32"])
+                                  "mqa_g32", "f32_d128", "f32_d64_paged"])
 def test_rows_written_by_the_caller(name):
     # the prefill goes straight into the natural-row caches through torch
     # indexing (no library call), as a KV manager that owns the pool would
