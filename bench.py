@@ -873,6 +873,9 @@ def main():
                 "kernel": ROOFLINE_KERNEL,
                 "avg_launch_us": kern_sec * 1e6, "bytes_per_launch": kern_bytes,
                 "launches": klaunch}
+    # HBM traffic over the algorithmic bytes (1.0: no byte fetched twice)
+    roofline["traffic_over_algorithmic"] = (roofline["traffic"] / kern_bytes
+                                            if roofline["traffic"] else None)
     log(f"kernel: {kern_sec * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
 
     # ---- the same step kernel on caches in the natural row layout
