@@ -10,7 +10,7 @@
 // runs once per query head, in a launch of its own, instead of in every
 // workgroup of the group:
 //
-//  match_kernel, one wave per query head: rotates the query (float64
+//  match_kernel, two waves per query head: rotates the query (float64
 //  angles, scaled by log2(e)/sqrt(d)) into bf16 hi/lo rows of the
 //  workspace, matches the pre-RoPE query against the ring and records the
 //  head's result (for the attention, the merge and the optional outputs);
@@ -44,21 +44,29 @@ __host__ __device__ inline uint16_t* wide_qrot(const StepArgs& a) {
 }
 
 // ========================================================= match kernel ==
+// Two waves per query head: wave w matches the head's ring slots w, w + 2,
+// ... and rotates half of the query's pairs; wave 0 keeps the better of the
+// two candidates (smaller distance, then the newer entry) and writes the
+// head's record and, on a hit, the matched entry's state.
 template <int D>
-__global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
+__global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
   using T = uint16_t;
-  constexpr int KMS = kMatchSlotsWhole;
+  constexpr int KMS = kMatchSlotsHalf;
   const int bh = blockIdx.x;
   const int b = bh / a.hq;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % 64;
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  __shared__ int best[2][5];   // per wave: d2 bits, age, p, n, ring pushes
   MatchIn<T, D, KMS> mi;
-  match_load<T, D, KMS>(a, bh, lane, 1, 0, mi);
+  match_load<T, D, KMS>(a, bh, lane, 2, half, mi);
   const int n0 = a.seq_lens[b];
   const bool append = a.k_new != nullptr && n0 >= 0 && n0 < a.geom.capacity;
   const int n = append ? n0 + 1 : n0;
   const int p_new = n - a.band > 0 ? n - a.band : 0;
   // rotate-half pairs (i, i + D/2) at position n - 1, float64 angle and
-  // rotation, scaled so that the attention can use exp2; hi and lo halves
+  // rotation, scaled so that the attention can use exp2; hi and lo halves.
+  // Both waves rotate every pair (so each consumes its loads) and store
+  // half of them.
   if (lane < D / 2) {
     float sn, cs;
     rope_sincos(n - 1, mi.inv, &sn, &cs);
@@ -66,16 +74,30 @@ __global__ __launch_bounds__(64) void match_kernel(StepArgs a) {
     const float sc = static_cast<float>(kLog2e / sqrt(static_cast<double>(D)));
     const float r1 = fmaf(x1, cs, -x2 * sn) * sc;
     const float r2 = fmaf(x2, cs, x1 * sn) * sc;
-    uint16_t* qh = wide_qrot(a) + static_cast<size_t>(bh) * 2 * D;
-    uint16_t* ql = qh + D;
-    const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
-    qh[lane] = h1;
-    qh[lane + D / 2] = h2;
-    ql[lane] = f32_to_bf16(r1 - bf16_to_f32(h1));
-    ql[lane + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
+    if (lane / (D / 4) == half) {
+      uint16_t* qh = wide_qrot(a) + static_cast<size_t>(bh) * 2 * D;
+      uint16_t* ql = qh + D;
+      const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
+      qh[lane] = h1;
+      qh[lane + D / 2] = h2;
+      ql[lane] = f32_to_bf16(r1 - bf16_to_f32(h1));
+      ql[lane + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
+    }
   }
-  const Best bst = match_best<T, D, KMS>(a, bh, lane, p_new, 1, 0, mi);
-  const HeadState hs = head_record(a, bst, mi.cnt, n);
+  const Best bst = match_best<T, D, KMS>(a, bh, lane, p_new, 2, half, mi);
+  if (lane == 0) {
+    best[half][0] = __float_as_int(bst.d2);
+    best[half][1] = bst.k;
+    best[half][2] = bst.p;
+    best[half][3] = bst.n;
+    best[half][4] = mi.cnt;
+  }
+  __syncthreads();
+  if (half != 0) return;
+  Best b0{__int_as_float(best[0][0]), best[0][1], best[0][2], best[0][3]};
+  const float d1 = __int_as_float(best[1][0]);
+  if (better_than(d1, best[1][1], b0.d2, b0.k)) b0 = Best{d1, best[1][1], best[1][2], best[1][3]};
+  const HeadState hs = head_record(a, b0, best[0][4], n);
   if (lane == 0) {
     a.heads[bh] = hs;
     if (a.match_ctx_out) a.match_ctx_out[bh] = hs.match_n;
@@ -477,8 +499,8 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
 }
 
 hipError_t launch_match_wide(const StepArgs& a, int d, hipStream_t st) {
-  if (d == 128) hipLaunchKernelGGL((match_kernel<128>), dim3(a.batch * a.hq), dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((match_kernel<64>), dim3(a.batch * a.hq), dim3(64), 0, st, a);
+  if (d == 128) hipLaunchKernelGGL((match_kernel<128>), dim3(a.batch * a.hq), dim3(128), 0, st, a);
+  else hipLaunchKernelGGL((match_kernel<64>), dim3(a.batch * a.hq), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
