@@ -147,7 +147,7 @@ typedef struct mac_ctx mac_ctx;
  *   to the library: write tokens only with mac_append_kv or mac_prefill_kv,
  *   read them back with mac_read_kv.
  * Both layouts give bitwise identical results; the tile layout spares the
- * step kernels an LDS transpose of each value tile.
+ * step kernels an LDS pass of each key and value tile.
  */
 size_t mac_kv_cache_bytes(const mac_config* cfg);  /* bytes of ONE of K, V   */
 size_t mac_ring_bytes(const mac_config* cfg);      /* opaque ring            */

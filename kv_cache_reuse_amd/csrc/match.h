@@ -24,39 +24,74 @@ constexpr int kMatchSlotsHalf = 5;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// ------------------------------------------------- natural-layout values --
-// Value tiles in the natural (row) layout arrive with lane (lg, c) holding
-// token c, elements [E (4 j + lg), +E) of block j: the order of the key
-// operand, not of the value operand.  The wave writes the tile to LDS rows of
-// its own and reads it back in the value operand order of the library's
-// tiles.  bf16 (16 rows of D + 8 elements; 16-byte aligned): vr[i] holds tokens
-// 4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element 4 th + r,
-// two per dword).  LDS accesses of one wave complete in order, so the reads
-// see the writes, and a later tile's writes follow this tile's reads.
+// -------------------------------------------------- natural-layout tiles --
+// A tile of the natural (row) layout is 16 rows of D elements, contiguous,
+// and loads like the library's tiles: 1 KiB per load, lane l of load j
+// holding 16-byte piece g = 64 j + l of the tile (row g / PR, piece g mod PR
+// of it, PR = D sizeof(T) / 16 pieces per row), so that every 128-byte line
+// arrives whole in one load.  Each streaming wave writes its K and its V tile,
+// as loaded, into LDS rows of its own and reads them back in the operand
+// order of the library's tiles:
+//  - K: lane (lg, c) takes piece 4 j + lg of row c as kr[j];
+//  - V, bf16 (rows of D + 8 elements, 16-byte aligned): vr[i] holds tokens
+//    4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element
+//    4 th + r, two per dword);
+//  - V, fp32 (rows of D + 4 floats, so that the reads of one element of 64
+//    lanes fall in 64 different banks): vr[i] holds tokens 4 lg .. 4 lg + 3
+//    of dim 16 i + c.
+// LDS accesses of one wave complete in order, so the reads see the writes,
+// and a later tile's writes follow this tile's reads.
 template <int D>
-struct VRows {
+struct KvRows {
   static constexpr int RS = D + 8;
   __attribute__((aligned(16))) uint16_t v[16 * RS];
 };
 
-// fp32 values: lane (lg, c) holds token c, elements [4 (4 j + lg), +4) of
-// block j (D / 16 blocks); rows of D + 4 floats (16-byte aligned; the reads
-// of one element of 64 lanes then fall in 64 different banks), read back
-// as vr[i] = tokens 4 lg .. 4 lg + 3 of dim 16 i + c, the value operand
-// order of the library's fp32 tiles.
 template <int D>
-struct VRowsF {
+struct KvRowsF {
   static constexpr int RS = D + 4;
   __attribute__((aligned(16))) float v[16 * RS];
 };
 
-template <int D>
-__device__ __forceinline__ void v_rows_to_operand(VRowsF<D>& rows, int lane, u4 (&vr)[D / 16]) {
-  constexpr int NL = D / 16;
-  constexpr int RS = VRowsF<D>::RS;
+// The NL loads of a tile, as loaded, into rows RS elements apart.
+template <typename ET, int RS, int NL>
+__device__ __forceinline__ void rows_store(ET* rows, int lane, const u4 (&x)[NL]) {
+  constexpr int E = 16 / (int)sizeof(ET);
+  constexpr int PR = 4 * NL;   // pieces per row: 16 rows of NL KiB / 16
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int g = 64 * j + lane;
+    *reinterpret_cast<u4*>(rows + (g / PR) * RS + E * (g % PR)) = x[j];
+  }
+}
+
+// Key operand order: kr[j] = piece 4 j + lg of row c.
+template <typename ET, int RS, int NL>
+__device__ __forceinline__ void rows_key_operand(const ET* rows, int lane, u4 (&kr)[NL]) {
+  constexpr int E = 16 / (int)sizeof(ET);
   const int lg = lane / 16, c = lane % 16;
 #pragma unroll
-  for (int j = 0; j < NL; ++j) *reinterpret_cast<u4*>(rows.v + c * RS + 4 * (4 * j + lg)) = vr[j];
+  for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(rows + c * RS + E * (4 * j + lg));
+}
+
+template <int D>
+__device__ __forceinline__ void k_rows_to_operand(KvRows<D>& rows, int lane, u4 (&kr)[D / 32]) {
+  rows_store<uint16_t, KvRows<D>::RS, D / 32>(rows.v, lane, kr);
+  rows_key_operand<uint16_t, KvRows<D>::RS, D / 32>(rows.v, lane, kr);
+}
+
+template <int D>
+__device__ __forceinline__ void k_rows_to_operand(KvRowsF<D>& rows, int lane, u4 (&kr)[D / 16]) {
+  rows_store<float, KvRowsF<D>::RS, D / 16>(rows.v, lane, kr);
+  rows_key_operand<float, KvRowsF<D>::RS, D / 16>(rows.v, lane, kr);
+}
+
+template <int D>
+__device__ __forceinline__ void v_rows_to_operand(KvRowsF<D>& rows, int lane, u4 (&vr)[D / 16]) {
+  constexpr int NL = D / 16;
+  constexpr int RS = KvRowsF<D>::RS;
+  const int lg = lane / 16, c = lane % 16;
+  rows_store<float, RS, NL>(rows.v, lane, vr);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int d = 16 * i + c;
@@ -65,26 +100,44 @@ __device__ __forceinline__ void v_rows_to_operand(VRowsF<D>& rows, int lane, u4 
   }
 }
 
+// bf16 values are read back with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): in each block of 16 lanes, lane 4 e + q supplies the
+// address of 4 consecutive elements and lane 4 q + r receives element r of
+// the addresses of lanes 4 e + q, e = 0 .. 3, as its elements 0 .. 3.  Lane
+// (lg, 4 e + q) therefore points at token 4 lg + e, dims 16 k + 4 q .. + 3,
+// and lane (lg, c) receives tokens 4 lg .. 4 lg + 3 of dim 16 k + c.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int D>
-__device__ __forceinline__ void v_rows_to_operand(VRows<D>& rows, int lane, u4 (&vr)[D / 32]) {
+__device__ __forceinline__ void v_rows_to_operand(KvRows<D>& rows, int lane, u4 (&vr)[D / 32]) {
   constexpr int NL = D / 32;
-  constexpr int RS = VRows<D>::RS;
-  const int lg = lane / 16, c = lane % 16;
-#pragma unroll
-  for (int j = 0; j < NL; ++j) *reinterpret_cast<u4*>(rows.v + c * RS + 8 * (4 * j + lg)) = vr[j];
+  constexpr int RS = KvRows<D>::RS;
+  rows_store<uint16_t, RS, NL>(rows.v, lane, vr);
+  const uint16_t* src = rows.v + (4 * (lane / 16) + (lane % 16) / 4) * RS + 4 * (lane % 4);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    uint32_t w[4];
+    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 32 * i));
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 32 * i + 16));
+    const u2 w0 = __builtin_bit_cast(u2, x0), w1 = __builtin_bit_cast(u2, x1);
+    vr[i] = u4{w0.x, w0.y, w1.x, w1.y};
+  }
+}
+
+// Patch of a natural-layout tile as loaded: row r of K and V (one of
+// D elements each, staged in LDS) replaces what the loads brought.
+template <typename ET, int NL>
+__device__ __forceinline__ void rows_patch(int lane, int r, const ET* pk, const ET* pv, u4 (&kr)[NL],
+                                           u4 (&vr)[NL]) {
+  constexpr int E = 16 / (int)sizeof(ET);
+  constexpr int PR = 4 * NL;
 #pragma unroll
-    for (int th = 0; th < 2; ++th)
-#pragma unroll
-      for (int rp = 0; rp < 2; ++rp) {
-        const int d = 16 * (2 * i + th) + c;
-        const uint32_t lo = rows.v[(4 * lg + 2 * rp) * RS + d];
-        const uint32_t hi = rows.v[(4 * lg + 2 * rp + 1) * RS + d];
-        w[2 * th + rp] = lo | (hi << 16);
-      }
-    vr[i] = u4{w[0], w[1], w[2], w[3]};
+  for (int j = 0; j < NL; ++j) {
+    const int g = 64 * j + lane;
+    if (g / PR == r) {
+      kr[j] = *reinterpret_cast<const u4*>(pk + E * (g % PR));
+      vr[j] = *reinterpret_cast<const u4*>(pv + E * (g % PR));
+    }
   }
 }
 

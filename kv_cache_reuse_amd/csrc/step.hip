@@ -89,9 +89,9 @@ __host__ __device__ constexpr int step_waves() {
 // group than one round fills): the slice-0 workgroup publishes its plan
 // start and second-round workgroups whose slice is empty leave early.  A
 // separate instantiation, so that one-round launches carry none of it.
-// NAT: caches in the natural (row) layout: keys load with row
-// offsets, and each value tile passes through the wave's LDS rows into the
-// value operand order.
+// NAT: caches in the natural (row) layout: tiles load like the library's
+// tiles, and each K and V tile passes through the wave's LDS rows into
+// operand order.
 template <typename T, int D, bool PAGED, bool WIDE, bool R2 = false, bool NAT = false>
 __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(StepArgs a) {
   constexpr int NWV = step_waves<T, D, WIDE>(); // waves per workgroup
@@ -105,8 +105,9 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   constexpr int NCT = D / 16;                   // 16-dim column tiles of O^T
 
   __shared__ Shared<D, NWB, WIDE ? kMaxGroup : 4> sh;
-  // natural rows: each streaming wave's LDS rows for its value tiles
-  using VR = std::conditional_t<BF, VRows<NAT ? D : 32>, VRowsF<NAT ? D : 32>>;
+  // natural rows: each streaming wave's LDS rows for its key and value tiles
+  using VR = std::conditional_t<BF, KvRows<NAT ? D : 32>, KvRowsF<NAT ? D : 32>>;
+  __shared__ VR krows[NAT ? NWB : 1];
   __shared__ VR vrows[NAT ? NWB : 1];
   // (padding ids of a chunked group get slice S: no plan gives it work, and
   // it writes nothing; no early return here, so that the compiler issues the
@@ -136,12 +137,11 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
   // rewritten per tile (a per-tile vector address can land on a register
   // that a load in flight still targets, and the compiler then waits for
   // every load).  The descriptor covers exactly the tile.
-  // (rows: lane (lg, c) reads token c's 16-byte piece 4 j + lg, block j
-  // 64 bytes further; a natural contiguous cache's last tile may hold fewer
-  // than 16 rows, and the descriptor then ends with them)
-  const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * (int)sizeof(T) + 16 * (lane / 16))
-                            : 16u * static_cast<uint32_t>(lane);
-  constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
+  // (a tile of either layout is 16 D sizeof(T) contiguous bytes; a natural
+  // contiguous cache's last tile may hold fewer than 16 rows, and the
+  // descriptor then ends with them)
+  const uint32_t loff = 16u * static_cast<uint32_t>(lane);
+  constexpr uint32_t kBlockStep = 1024u;
   // cpol: the loads' cache policy (kCachePolicyKeep or kCachePolicyStream),
   // a compile-time constant of the instruction
   auto load_tile_p = [&](auto cpol, int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
@@ -357,15 +357,12 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
 
     auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) __attribute__((always_inline)) {
       if (patcher && tt == tnew) {
-        // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
-        // (rows: V of token c, like K)
-        if (col == rnew) {
+        // rows: the tile as loaded; tiles: lane (lg, c) holds K of token c
+        // and V of tokens 4 lg .. 4 lg + 3
+        if constexpr (NAT) rows_patch<T, NL>(lane, rnew, pk, pv, kr, vr);
+        if (!NAT && col == rnew) {
 #pragma unroll
           for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(pk + E * (4 * j + lg));
-          if constexpr (NAT) {
-#pragma unroll
-            for (int j = 0; j < NL; ++j) vr[j] = *reinterpret_cast<const u4*>(pv + E * (4 * j + lg));
-          }
         }
         if (!NAT && lg == rnew / 4) {
 #pragma unroll
@@ -392,7 +389,10 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
             }
         }
       }
-      if constexpr (NAT) v_rows_to_operand<D>(vrows[wave], lane, vr);
+      if constexpr (NAT) {
+        k_rows_to_operand<D>(krows[wave], lane, kr);
+        v_rows_to_operand<D>(vrows[wave], lane, vr);
+      }
       // ---- S = K Q^T: lane holds tokens 4 lg + r of head col
       v4f s = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF) {
@@ -522,9 +522,8 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     // hit or miss.  (Each policy has its own copy of the loop, chosen
     // before it, so no load sits under a branch inside it; fp32 d128 at
     // two waves per SIMD has no registers for the second copy and streams
-    // every slice with the non-temporal policy.  Natural rows keep the
-    // default: a row load covers half of each 128-byte line and the next
-    // load the other half, which a line not kept would fetch twice.)
+    // every slice with the non-temporal policy.  Natural rows load whole
+    // lines too, so they take the same policies.)
     auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
@@ -547,9 +546,7 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
     };
     constexpr bool kTwoLoops = !(sizeof(T) == 4 && D == 128 && NWV > 4);
     if (nt > 0) {
-      if constexpr (NAT) {
-        stream(kKeep);
-      } else if constexpr (kTwoLoops) {
+      if constexpr (kTwoLoops) {
         if (slice_is_pre(p, slice)) stream(kStream);
         else stream(kKeep);
       } else {

@@ -133,8 +133,9 @@ struct WideShared {
 // ...).  With no match to do, the workgroup has no other waves: at one wave
 // per SIMD each wave holds both column tiles' queries and accumulators and
 // two KV tiles in flight in registers.
-// NAT: caches in the natural (row) layout: keys load with row offsets and
-// each value tile passes through the wave's LDS rows into operand order.
+// NAT: caches in the natural (row) layout: tiles load like the library's
+// tiles, and each K and V tile passes through the wave's LDS rows into
+// operand order.
 template <int D, bool PAGED, int NWB, bool NAT>
 __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   using T = uint16_t;
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   constexpr int NC = kWideCols;
 
   __shared__ WideShared<D, NWB> sh;
-  __shared__ VRows<NAT ? D : 32> vrows[NAT ? NWB : 1];
+  __shared__ KvRows<NAT ? D : 32> krows[NAT ? NWB : 1];
+  __shared__ KvRows<NAT ? D : 32> vrows[NAT ? NWB : 1];
   int grp, slice;
   step_coords(blockIdx.x, a.batch * a.hkv, a.nchunk, a.part.S, &grp, &slice);
   const int b = grp / a.hkv, kvh = grp % a.hkv;
@@ -161,9 +163,11 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
   geom.paged = PAGED ? 1 : 0;
   geom.natural = NAT ? 1 : 0;
   geom.d = D;
-  const uint32_t loff = NAT ? static_cast<uint32_t>((lane % 16) * D * 2 + 16 * (lane / 16))
-                            : 16u * static_cast<uint32_t>(lane);
-  constexpr uint32_t kBlockStep = NAT ? 64u : 1024u;
+  // (a tile of either layout is 32 D contiguous bytes; a natural contiguous
+  // cache's last tile may hold fewer than 16 rows, and the descriptor then
+  // ends with them)
+  const uint32_t loff = 16u * static_cast<uint32_t>(lane);
+  constexpr uint32_t kBlockStep = 1024u;
   auto load_tile_p = [&](auto cpol, int tt, u4 (&kk)[NL], u4 (&vv)[NL]) {
     const int64_t base = tile_base(geom, a.page_table, b, kvr, tt);
     const int bytes = (NAT && !PAGED ? tile_rows(geom, tt) : kTile) * D * 2;
@@ -273,15 +277,12 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
 
     auto process = [&](int tt, u4 (&kr)[NL], u4 (&vr)[NL]) __attribute__((always_inline)) {
       if (patcher && tt == tnew) {
-        // lane (lg, c) holds K of token c and V of tokens 4 lg .. 4 lg + 3
-        // (rows: V of token c, like K)
-        if (col == rnew) {
+        // rows: the tile as loaded; tiles: lane (lg, c) holds K of token c
+        // and V of tokens 4 lg .. 4 lg + 3
+        if constexpr (NAT) rows_patch<T, NL>(lane, rnew, pk, pv, kr, vr);
+        if (!NAT && col == rnew) {
 #pragma unroll
           for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(pk + E * (4 * j + lg));
-          if constexpr (NAT) {
-#pragma unroll
-            for (int j = 0; j < NL; ++j) vr[j] = *reinterpret_cast<const u4*>(pv + E * (4 * j + lg));
-          }
         }
         if (!NAT && lg == rnew / 4) {
 #pragma unroll
@@ -300,7 +301,10 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
             }
         }
       }
-      if constexpr (NAT) v_rows_to_operand<D>(vrows[wave], lane, vr);
+      if constexpr (NAT) {
+        k_rows_to_operand<D>(krows[wave], lane, kr);
+        v_rows_to_operand<D>(vrows[wave], lane, vr);
+      }
       // ---- S = K Q^T for both column tiles: lane holds tokens 4 lg + r.
       // One K = 32 product per 1 KiB block: a lane's 16-byte piece (8 dims
       // of its token) is its A operand as loaded, and the same 8 dims of
@@ -398,8 +402,7 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
     const int nt = wave < NWB && tw < t1 ? (t1 - tw + NWB - 1) / NWB : 0;
     // slices before p_new stream with the non-temporal policy, the band and
     // the tail (read again by the next steps) with the default one; one
-    // copy of the loop per policy (natural rows keep the default: a row
-    // load covers half of each 128-byte line, the next load the other half)
+    // copy of the loop per policy (natural rows load whole lines too)
     auto stream = [&](auto cpol) __attribute__((always_inline)) {
       u4 kB[NL], vB[NL];
       if (tw != tspec) load_tile_p(cpol, tw, kA, vA);
@@ -421,12 +424,8 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
       }
     };
     if (nt > 0) {
-      if constexpr (NAT) {
-        stream(kKeep);
-      } else {
-        if (slice_is_pre(p, slice)) stream(kStream);
-        else stream(kKeep);
-      }
+      if (slice_is_pre(p, slice)) stream(kStream);
+      else stream(kKeep);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
