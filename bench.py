@@ -60,7 +60,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_step_kernel_8b_128k.js
 # sources the step kernel is compiled from: the stored counter figures are
 # only valid for the kernel they were taken on
 KERNEL_SRCS = [os.path.join(ROOT, "kv_cache_reuse_amd", "csrc", f)
-               for f in ("step.hip", "match.h", "mac_dev.h")]
+               for f in ("step.hip", "match.h", "mac_dev.h", "rows_map.h")]
 ROOFLINE_KERNEL = "mac::step_kernel<bf16,128,contiguous>"
 COPY_CAL_BYTES = 512 * 1024 * 1024
 

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "mac_dev.h"
+#include "rows_map.h"
 
 namespace mac {
 
@@ -25,31 +26,23 @@ constexpr int kMatchSlotsHalf = 5;
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // -------------------------------------------------- natural-layout tiles --
-// A tile of the natural (row) layout is 16 rows of D elements, contiguous,
-// and loads like the library's tiles: 1 KiB per load, lane l of load j
-// holding 16-byte piece g = 64 j + l of the tile (row g / PR, piece g mod PR
-// of it, PR = D sizeof(T) / 16 pieces per row), so that every 128-byte line
-// arrives whole in one load.  Each streaming wave writes its K and its V tile,
-// as loaded, into LDS rows of its own and reads them back in the operand
-// order of the library's tiles:
-//  - K: lane (lg, c) takes piece 4 j + lg of row c as kr[j];
-//  - V, bf16 (rows of D + 8 elements, 16-byte aligned): vr[i] holds tokens
-//    4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element
-//    4 th + r, two per dword);
-//  - V, fp32 (rows of D + 4 floats, so that the reads of one element of 64
-//    lanes fall in 64 different banks): vr[i] holds tokens 4 lg .. 4 lg + 3
-//    of dim 16 i + c.
-// LDS accesses of one wave complete in order, so the reads see the writes,
-// and a later tile's writes follow this tile's reads.
+// A tile of the natural (row) layout loads like the library's tiles (1 KiB
+// per wave load, every 128-byte line whole in one load); each streaming
+// wave writes its K and V tile, as loaded, into LDS rows of its own and reads
+// them back in the operand order of the library's tiles.  The lane maps are
+// in rows_map.h.  LDS accesses of one wave complete in order, so the reads
+// see the writes, and a later tile's writes follow this tile's reads.
 template <int D>
 struct KvRows {
-  static constexpr int RS = D + 8;
+  static constexpr int RS = D + kRowsPadBf16;
   __attribute__((aligned(16))) uint16_t v[16 * RS];
 };
 
+// (fp32 rows of D + 4: the reads of one element of 64 lanes fall in 64
+// different banks)
 template <int D>
 struct KvRowsF {
-  static constexpr int RS = D + 4;
+  static constexpr int RS = D + kRowsPadF32;
   __attribute__((aligned(16))) float v[16 * RS];
 };
 
@@ -59,19 +52,17 @@ __device__ __forceinline__ void rows_store(ET* rows, int lane, const u4 (&x)[NL]
   constexpr int E = 16 / (int)sizeof(ET);
   constexpr int PR = 4 * NL;   // pieces per row: 16 rows of NL KiB / 16
 #pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    const int g = 64 * j + lane;
-    *reinterpret_cast<u4*>(rows + (g / PR) * RS + E * (g % PR)) = x[j];
-  }
+  for (int j = 0; j < NL; ++j)
+    *reinterpret_cast<u4*>(rows + rows_load_row(j, lane, PR) * RS + E * rows_load_piece(j, lane, PR)) = x[j];
 }
 
-// Key operand order: kr[j] = piece 4 j + lg of row c.
+// Key operand order.
 template <typename ET, int RS, int NL>
 __device__ __forceinline__ void rows_key_operand(const ET* rows, int lane, u4 (&kr)[NL]) {
   constexpr int E = 16 / (int)sizeof(ET);
-  const int lg = lane / 16, c = lane % 16;
 #pragma unroll
-  for (int j = 0; j < NL; ++j) kr[j] = *reinterpret_cast<const u4*>(rows + c * RS + E * (4 * j + lg));
+  for (int j = 0; j < NL; ++j)
+    kr[j] = *reinterpret_cast<const u4*>(rows + rows_key_row(lane) * RS + E * rows_key_piece(j, lane));
 }
 
 template <int D>
@@ -86,6 +77,7 @@ __device__ __forceinline__ void k_rows_to_operand(KvRowsF<D>& rows, int lane, u4
   rows_key_operand<float, KvRowsF<D>::RS, D / 16>(rows.v, lane, kr);
 }
 
+// fp32 values: vr[i] = tokens 4 lg .. 4 lg + 3 of dim 16 i + c.
 template <int D>
 __device__ __forceinline__ void v_rows_to_operand(KvRowsF<D>& rows, int lane, u4 (&vr)[D / 16]) {
   constexpr int NL = D / 16;
@@ -100,12 +92,9 @@ __device__ __forceinline__ void v_rows_to_operand(KvRowsF<D>& rows, int lane, u4
   }
 }
 
-// bf16 values are read back with gfx950's transposing LDS read
-// (ds_read_b64_tr_b16): in each block of 16 lanes, lane 4 e + q supplies the
-// address of 4 consecutive elements and lane 4 q + r receives element r of
-// the addresses of lanes 4 e + q, e = 0 .. 3, as its elements 0 .. 3.  Lane
-// (lg, 4 e + q) therefore points at token 4 lg + e, dims 16 k + 4 q .. + 3,
-// and lane (lg, c) receives tokens 4 lg .. 4 lg + 3 of dim 16 k + c.
+// bf16 values, through the transposing LDS read: vr[i] holds tokens
+// 4 lg .. 4 lg + 3 of dims 16 (2 i + th) + c for th = 0, 1 (element
+// 4 th + r, two per dword).
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -114,7 +103,7 @@ __device__ __forceinline__ void v_rows_to_operand(KvRows<D>& rows, int lane, u4 
   constexpr int NL = D / 32;
   constexpr int RS = KvRows<D>::RS;
   rows_store<uint16_t, RS, NL>(rows.v, lane, vr);
-  const uint16_t* src = rows.v + (4 * (lane / 16) + (lane % 16) / 4) * RS + 4 * (lane % 4);
+  const uint16_t* src = rows.v + tr16_row(lane) * RS + tr16_col(lane);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(src + 32 * i));
@@ -133,10 +122,9 @@ __device__ __forceinline__ void rows_patch(int lane, int r, const ET* pk, const 
   constexpr int PR = 4 * NL;
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    const int g = 64 * j + lane;
-    if (g / PR == r) {
-      kr[j] = *reinterpret_cast<const u4*>(pk + E * (g % PR));
-      vr[j] = *reinterpret_cast<const u4*>(pv + E * (g % PR));
+    if (rows_load_row(j, lane, PR) == r) {
+      kr[j] = *reinterpret_cast<const u4*>(pk + E * rows_load_piece(j, lane, PR));
+      vr[j] = *reinterpret_cast<const u4*>(pv + E * rows_load_piece(j, lane, PR));
     }
   }
 }

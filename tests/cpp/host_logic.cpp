@@ -1,7 +1,9 @@
 // Host checks of libmac's integer logic, compiled from the library's own
-// header: the KV tile permutations are bijections onto the tile, and the
-// split-K plan partitions the fresh range [lo, n) into slices that never
-// straddle p_new, with every slice non-empty and at most max_slices of them.
+// headers: the KV tile permutations are bijections onto the tile; the
+// natural-row tiles' loads, LDS rows and read-back give every lane the
+// elements the tile layout gives it; and the split-K plan partitions the
+// fresh range [lo, n) into slices that never straddle p_new, with every
+// slice non-empty and at most max_slices of them.
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
@@ -10,6 +12,7 @@
 
 #include "../../kv_cache_reuse_amd/csrc/mac_dev.h"
 #include "../../kv_cache_reuse_amd/csrc/merge_map.h"
+#include "../../kv_cache_reuse_amd/csrc/rows_map.h"
 
 static int fails = 0;
 #define CHECK(c, ...)                         \
@@ -169,11 +172,85 @@ void check_merge_coords(int batch, int hkv, int group, int parts, int S) {
   for (int i = 0; i < n; ++i) CHECK(seen[i] == 1, "merge (head, part) %d taken %d times", i, seen[i]);
 }
 
+// Natural-row tiles.  A tile's element (token, dim) sits at token * D + dim
+// of the row tile and at k_tile_offset / v_tile_offset of a library tile; a
+// wave load j gives lane l the 16 bytes at element E (64 j + l) of either.
+// The row path writes each load's piece into the LDS rows and reads the
+// operands back (bf16 values through a model of the transposing LDS read:
+// in each block of 16 lanes, lane B + i takes element i mod 4 of the 4 at
+// the address of lane B + 4 r + i / 4 as its element r); every operand
+// element must be the one the tile path loads into that lane and slot.
+template <typename T>
+void check_rows(int D) {
+  const int E = 16 / (int)sizeof(T);
+  const int NL = D * (int)sizeof(T) / 64;
+  const int PR = 4 * NL;
+  const int RS = D + (sizeof(T) == 2 ? mac::kRowsPadBf16 : mac::kRowsPadF32);
+  std::vector<int> kinv(16 * D, -1), vinv(16 * D, -1);
+  for (int tok = 0; tok < 16; ++tok)
+    for (int d = 0; d < D; ++d) {
+      kinv[mac::k_tile_offset<T>(tok, d)] = tok * D + d;
+      vinv[mac::v_tile_offset<T>(tok, d)] = tok * D + d;
+    }
+  std::vector<int> lds(16 * RS, -1);
+  for (int j = 0; j < NL; ++j)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int row = mac::rows_load_row(j, lane, PR), piece = mac::rows_load_piece(j, lane, PR);
+      CHECK(row >= 0 && row < 16 && piece >= 0 && piece < PR, "load %d lane %d -> row %d piece %d", j, lane, row, piece);
+      for (int e = 0; e < E; ++e) {
+        const int label = E * (64 * j + lane) + e;   // the row tile's element there
+        CHECK(label == row * D + E * piece + e, "load %d lane %d e %d: row %d piece %d", j, lane, e, row, piece);
+        CHECK(lds[row * RS + E * piece + e] == -1, "LDS slot written twice (row %d piece %d)", row, piece);
+        lds[row * RS + E * piece + e] = label;
+      }
+    }
+  for (int j = 0; j < NL; ++j)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int e = 0; e < E; ++e) {
+        const int got = lds[mac::rows_key_row(lane) * RS + E * mac::rows_key_piece(j, lane) + e];
+        CHECK(got == kinv[E * (64 * j + lane) + e], "key j %d lane %d e %d: %d vs %d (D %d)", j, lane, e, got,
+              kinv[E * (64 * j + lane) + e], D);
+      }
+  for (int i = 0; i < NL; ++i)
+    for (int lane = 0; lane < 64; ++lane) {
+      if (sizeof(T) == 2) {
+        const int B = lane & ~15, ii = lane % 16;
+        for (int th = 0; th < 2; ++th)
+          for (int r = 0; r < 4; ++r) {
+            const int src = B + 4 * r + ii / 4;
+            const int col = 32 * i + 16 * th + mac::tr16_col(src);
+            CHECK(col + 3 < D, "transposing read past the row (col %d, D %d)", col, D);
+            const int got = lds[mac::tr16_row(src) * RS + col + ii % 4];
+            const int want = vinv[E * (64 * i + lane) + 4 * th + r];
+            CHECK(got == want, "value i %d lane %d th %d r %d: %d vs %d (D %d)", i, lane, th, r, got, want, D);
+          }
+      } else {
+        for (int r = 0; r < 4; ++r) {
+          const int got = lds[(4 * (lane / 16) + r) * RS + 16 * i + lane % 16];
+          const int want = vinv[4 * (64 * i + lane) + r];
+          CHECK(got == want, "value i %d lane %d r %d: %d vs %d (D %d)", i, lane, r, got, want, D);
+        }
+      }
+    }
+  // the fused-append patch of row r touches each of its pieces once
+  for (int r = 0; r < 16; ++r) {
+    std::vector<int> seen(PR, 0);
+    for (int j = 0; j < NL; ++j)
+      for (int lane = 0; lane < 64; ++lane)
+        if (mac::rows_load_row(j, lane, PR) == r) seen[mac::rows_load_piece(j, lane, PR)]++;
+    for (int p = 0; p < PR; ++p) CHECK(seen[p] == 1, "patch of row %d: piece %d taken %d times", r, p, seen[p]);
+  }
+}
+
 int main() {
   check_tiles<uint16_t>(64);
   check_tiles<uint16_t>(128);
   check_tiles<float>(64);
   check_tiles<float>(128);
+  check_rows<uint16_t>(64);
+  check_rows<uint16_t>(128);
+  check_rows<float>(64);
+  check_rows<float>(128);
   std::mt19937 rng(123);
   const int Ss[] = {2, 3, 8, 16, 34, 128, 1024};
   for (int it = 0; it < 200000; ++it) {
