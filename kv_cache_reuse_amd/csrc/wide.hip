@@ -483,15 +483,17 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
       a.part.ml[(pbase + tid) * 2 + 1] = L;
     }
     __syncthreads();
-    constexpr int RPP = NTH / D;                  // head rows per pass
-#pragma unroll 4
-    for (int h0 = 0; h0 < G; h0 += RPP) {
-      const int hh = h0 + tid / D, dim = tid % D;
-      if (hh < G) {
-        float o = 0.f;
+    // four dims per thread: 128-bit LDS reads of the waves' rows and one
+    // 128-bit store of the sum
+    constexpr int RPP = NTH / (D / 4);            // head rows per pass
 #pragma unroll
-        for (int w = 0; w < NWB; ++w) o += sh.sc[w][hh] * sh.o[w][hh][dim];
-        a.part.o[(pbase + hh) * D + dim] = o;
+    for (int h0 = 0; h0 < kWideHeads; h0 += RPP) {
+      const int hh = h0 + tid / (D / 4), d4 = 4 * (tid % (D / 4));
+      if (hh < G) {
+        v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NWB; ++w) o += sh.sc[w][hh] * *reinterpret_cast<const v4f*>(&sh.o[w][hh][d4]);
+        *reinterpret_cast<v4f*>(&a.part.o[(pbase + hh) * D + d4]) = o;
       }
     }
   }
