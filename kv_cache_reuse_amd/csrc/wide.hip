@@ -114,6 +114,9 @@ __global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kWideCols = 2;                   // 16-head column tiles per workgroup
+// Lazy rescaling threshold of the online softmax, log2 units: the largest
+// factor a weight may exceed 1 by is 2^8.
+constexpr float kLazyRescale = 8.f;
 constexpr int kWideHeads = 16 * kWideCols;     // query heads a workgroup attends for
 
 template <int D, int NWB>
@@ -352,21 +355,39 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
           vr[i].w &= m23;
         }
       }
-      // ---- online softmax per head, base 2; P split into bf16 hi/lo
+      // ---- online softmax per head, base 2; P split into bf16 hi/lo.
+      // The reference maximum m moves only when a tile's maximum passes it
+      // by more than kLazyRescale: the weights exp2(s - m) then stay below
+      // 2^kLazyRescale, (o, m, l) stays a consistent state, and most tiles
+      // skip rescaling the accumulators (with 32 heads some head's maximum
+      // grows on nearly every tile, and each rescale moves 64 accumulator
+      // registers through the VALU).
+      // Each lane tests its own four scores; only when one of the wave's
+      // scores passes its reference by more than kLazyRescale (one ballot,
+      // a branch the whole wave takes or skips) does the wave form each
+      // head's tile maximum across the four lane rows and rescale the heads
+      // whose maximum passed.
       v4s ph[NC], pl[NC];
+      bool up_any = false;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        float mx = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float mnew = fmaxf(m[c], mx);
-        if (mnew > m[c]) {
-          const float alpha = fast_exp2(m[c] - mnew);
+      for (int c = 0; c < NC; ++c)
+        up_any = up_any || fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3])) > m[c] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(up_any) != 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          float mx = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
+          mx = fmaxf(mx, shfl_xor_f(mx, 16));
+          mx = fmaxf(mx, shfl_xor_f(mx, 32));
+          const bool up = mx > m[c] + kLazyRescale;   // the same in a head's four lanes
+          const float alpha = up ? fast_exp2(m[c] - mx) : 1.f;
 #pragma unroll
           for (int i = 0; i < NCT; ++i) acc[c][i] *= alpha;
           lsum[c] *= alpha;
-          m[c] = mnew;
+          m[c] = up ? mx : m[c];
         }
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
         const float mref = m[c] == neg_inf() ? 0.f : m[c];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
