@@ -57,6 +57,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // differences of maxima.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lazy rescaling threshold of the step kernels' online softmax, log2 units:
+// a head's reference maximum moves only when a score passes it by more than
+// this, so a weight exp2(s - m) stays below 2^8.
+constexpr float kLazyRescale = 8.f;
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ __forceinline__ static float load(const float* p) { return *p; }

@@ -447,17 +447,22 @@ __global__ __launch_bounds__((64 * step_waves<T, D, WIDE>())) void step_kernel(S
         }
       }
 
-      // ---- online softmax, base 2
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      if (mnew > m) {
-        const float alpha = fast_exp2(m - mnew);
+      // ---- online softmax, base 2, with a lazy reference: each lane tests
+      // its four scores against its head's reference m, and only when one of
+      // the wave's scores passes it by more than kLazyRescale (one ballot, a
+      // branch the whole wave takes or skips) does the wave form the heads'
+      // tile maxima across the lane rows and rescale the heads whose maximum
+      // passed.  Weights exp2(s - m) stay below 2^kLazyRescale.
+      const float lmx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      if (__builtin_amdgcn_ballot_w64(lmx > m + kLazyRescale) != 0) {
+        float mx = fmaxf(lmx, shfl_xor_f(lmx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const bool up = mx > m + kLazyRescale;   // the same in a head's four lanes
+        const float alpha = up ? fast_exp2(m - mx) : 1.f;
 #pragma unroll
         for (int i = 0; i < NCT; ++i) acc[i] *= alpha;
         lsum *= alpha;
-        m = mnew;
+        m = up ? mx : m;
       }
       const float mref = m == neg_inf() ? 0.f : m;
       float pr[4];

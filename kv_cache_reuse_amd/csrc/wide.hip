@@ -114,9 +114,6 @@ __global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kWideCols = 2;                   // 16-head column tiles per workgroup
-// Lazy rescaling threshold of the online softmax, log2 units: the largest
-// factor a weight may exceed 1 by is 2^8.
-constexpr float kLazyRescale = 8.f;
 constexpr int kWideHeads = 16 * kWideCols;     // query heads a workgroup attends for
 
 template <int D, int NWB>
