@@ -262,6 +262,37 @@ def test_nan_query_poisons_only_its_head():
     assert_report(rep, "nan_head", 0)
 
 
+# Keys whose scale grows along the sequence (about 26x at 1500 keys,
+# scores up to about 100 in log2 units), with two slices per KV group, so
+# that each streaming wave walks a dozen tiles or more of rising scale: a
+# head's tile maximum keeps passing the softmax reference the step kernels
+# hold by more than 2^8, and the lazy rescale (a ballot, then the cross-row
+# maximum and the accumulators' rescale) runs several times in every wave.
+# One case keeps the default slice count (many short slices), so partial
+# states with references of every size meet in the merge and the ring.
+RAMP = {
+    "ramp_narrow": ("8b_32k", dict(context=1500, steps=24, p_jump=0.3), 2),
+    "ramp_narrow_default_slices": ("8b_32k", dict(context=1500, steps=24, p_jump=0.3), 0),
+    "ramp_g8": ("70b_128k", dict(batch=2, context=1300, steps=16, outlier_p=0.0), 2),
+    "ramp_mqa_wide": ("8b_32k", dict(n_kv_heads=1, context=1700, steps=16, p_jump=0.3), 2),
+    "ramp_paged": ("paged_b8", dict(batch=2, ctx_range=(900, 1600), steps=12), 2),
+    "ramp_f32": ("tiny", dict(context=1400, steps=24), 2),
+}
+
+
+@pytest.mark.parametrize("name", list(RAMP))
+def test_growing_key_scale_every_step(name):
+    base, kw, slices = RAMP[name]
+    w = workload(base, **kw)
+    inp = make_inputs(w)
+    L = inp.k.shape[2]
+    ramp = 1.0 + torch.arange(L, dtype=torch.float32) / 60.0
+    inp.k = (inp.k.float() * ramp[None, None, :, None]).to(inp.k.dtype)
+    gpu = run_gpu(w, inp, max_slices=slices)
+    rep = check_groups(w, inp, gpu, all_groups(w))
+    assert_report(rep, name)
+
+
 # ---------------------------------------------------------------------------
 # full sizes, launch configuration of the benchmark, every KV group and step
 # ---------------------------------------------------------------------------
