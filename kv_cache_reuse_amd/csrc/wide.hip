@@ -85,6 +85,28 @@ __global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
     }
   }
   const Best bst = match_best<T, D, KMS>(a, bh, lane, p_new, 2, half, mi);
+  // A wave whose best candidate is under tau loads that entry's state now:
+  // the load overlaps the exchange of the two waves' candidates, and on a
+  // hit the winning wave writes the state from its registers.
+  constexpr int EPL = D / 16;
+  const RingView& R = a.ring;
+  const bool own_hit = bst.k >= 0 && bst.d2 < a.tau2;
+  const int own_slot = own_hit ? (mi.cnt - 1 - bst.k) % R.slots : 0;
+  float ro[EPL];
+  float2 rml = make_float2(0.f, 0.f);
+  if (own_hit) {
+    const size_t re = (size_t)bh * R.slots + own_slot;
+    const float* src = R.o + re * D + EPL * (lane % 16);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + e);
+      ro[e] = x.x;
+      ro[e + 1] = x.y;
+      ro[e + 2] = x.z;
+      ro[e + 3] = x.w;
+    }
+    rml = reinterpret_cast<const float2*>(R.ml)[re];
+  }
   if (lane == 0) {
     best[half][0] = __float_as_int(bst.d2);
     best[half][1] = bst.k;
@@ -93,20 +115,33 @@ __global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
     best[half][4] = mi.cnt;
   }
   __syncthreads();
-  if (half != 0) return;
+  // both waves take the same decision: the better candidate (two slots
+  // never tie in both distance and age)
   Best b0{__int_as_float(best[0][0]), best[0][1], best[0][2], best[0][3]};
+  int win = 0;
   const float d1 = __int_as_float(best[1][0]);
-  if (better_than(d1, best[1][1], b0.d2, b0.k)) b0 = Best{d1, best[1][1], best[1][2], best[1][3]};
+  if (better_than(d1, best[1][1], b0.d2, b0.k)) {
+    b0 = Best{d1, best[1][1], best[1][2], best[1][3]};
+    win = 1;
+  }
   const HeadState hs = head_record(a, b0, best[0][4], n);
-  if (lane == 0) {
+  if (half == 0 && lane == 0) {
     a.heads[bh] = hs;
     if (a.match_ctx_out) a.match_ctx_out[bh] = hs.match_n;
     if (a.dist_out) a.dist_out[bh] = hs.dist;
   }
-  if (hs.hit) {
-    const size_t re = static_cast<size_t>(bh) * a.ring.slots + hs.slot;
-    for (int e = lane; e < D; e += 64) a.reuse_o[static_cast<size_t>(bh) * D + e] = a.ring.o[re * D + e];
-    if (lane < 2) a.reuse_ml[static_cast<size_t>(bh) * 2 + lane] = a.ring.ml[re * 2 + lane];
+  // on a hit the winner's own best is the matched entry, loaded above
+  if (hs.hit && half == win) {
+    if (lane < 16) {
+      float* dst = a.reuse_o + (size_t)bh * D + EPL * lane;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(ro[e], ro[e + 1], ro[e + 2], ro[e + 3]);
+    }
+    if (lane == 0) {
+      a.reuse_ml[(size_t)bh * 2] = rml.x;
+      a.reuse_ml[(size_t)bh * 2 + 1] = rml.y;
+    }
   }
 }
 
