@@ -45,9 +45,9 @@ __host__ __device__ inline uint16_t* wide_qrot(const StepArgs& a) {
 
 // ========================================================= match kernel ==
 // Two waves per query head: wave w matches the head's ring slots w, w + 2,
-// ... and rotates half of the query's pairs; wave 0 keeps the better of the
-// two candidates (smaller distance, then the newer entry) and writes the
-// head's record and, on a hit, the matched entry's state.
+// ... and rotates half of the query's pairs; both take the better of the two
+// candidates (smaller distance, then the newer entry), wave 0 writes the
+// head's record and, on a hit, the winning wave the matched entry's state.
 template <int D>
 __global__ __launch_bounds__(128) void match_kernel(StepArgs a) {
   using T = uint16_t;
@@ -388,17 +388,16 @@ __global__ __launch_bounds__(64 * NWB) void wide_step_kernel(StepArgs a) {
         }
       }
       // ---- online softmax per head, base 2; P split into bf16 hi/lo.
-      // The reference maximum m moves only when a tile's maximum passes it
-      // by more than kLazyRescale: the weights exp2(s - m) then stay below
+      // The reference maximum m moves only when a score passes it by more
+      // than kLazyRescale: the weights exp2(s - m) then stay below
       // 2^kLazyRescale, (o, m, l) stays a consistent state, and most tiles
       // skip rescaling the accumulators (with 32 heads some head's maximum
       // grows on nearly every tile, and each rescale moves 64 accumulator
-      // registers through the VALU).
-      // Each lane tests its own four scores; only when one of the wave's
-      // scores passes its reference by more than kLazyRescale (one ballot,
-      // a branch the whole wave takes or skips) does the wave form each
-      // head's tile maximum across the four lane rows and rescale the heads
-      // whose maximum passed.
+      // registers through the VALU).  Each lane tests its own four scores;
+      // only on a ballot that one of the wave's scores passed (a branch the
+      // whole wave takes or skips) does the wave form each head's tile
+      // maximum across the four lane rows and rescale the heads whose
+      // maximum passed.
       v4s ph[NC], pl[NC];
       bool up_any = false;
 #pragma unroll
