@@ -56,6 +56,11 @@ SMALL = {
     "mqa_g64": ("8b_32k", dict(n_q_heads=64, n_kv_heads=1, context=1800, steps=16)),
     "g20": ("8b_32k", dict(n_q_heads=40, n_kv_heads=2, context=1200, steps=16)),
     "mqa_paged": ("paged_b8", dict(batch=2, n_kv_heads=1, ctx_range=(500, 1200), steps=12)),
+    # wide-path match over windows of two and three rounds of slots (the
+    # matched entry's state then comes from a later round)
+    "mqa_w64": ("8b_32k", dict(n_kv_heads=1, context=1300, steps=80, window=64, p_jump=0.2)),
+    "g20_w100": ("8b_32k", dict(n_q_heads=40, n_kv_heads=2, context=900, steps=120, window=100,
+                               p_jump=0.2)),
     # every remaining (dtype, d, paged, wide) instantiation of the step kernel
     "f32_d128_wide": ("tiny", dict(head_dim=128, n_q_heads=16, n_kv_heads=2, context=1100, steps=16,
                                    tau=0.5 * math.sqrt(128))),
